@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Throughput of the fused W8A8 INT8 linear on one MI355X.
+
+One step = one pass of the whole hot path over the 1024px DiT MLP workload
+(4096 tokens, hidden 3072, MLP width 12288), on synthetic seeded inputs that
+are resident in HBM before timing starts:
+  1. per-token quantization of the up-proj input X [4096, 3072]
+  2. int8 GEMM + dequant/bias epilogue, up-proj   (M=4096, K=3072,  N=12288)
+  3. GELU + per-token quantization of R [4096, 12288] (the down-proj input is
+     the GELU of a random bf16 tensor with 1% outlier channels x20)
+  4. int8 GEMM + dequant/bias epilogue, down-proj (M=4096, K=12288, N=3072)
+Steps 1+2 are exactly what w8a8_linear enqueues; they are issued as the two
+entry points so that HIP events can bracket the GEMM kernel alone.  Weight
+quantization (per output channel) is offline and not timed.  Weights rotate
+over several copies so that the 256 MB last-level cache cannot hold them
+across steps.
+
+Output: one JSON line.  `value` is int8 tera-operations per second over the
+whole step (2*M*N*K per GEMM).  `roofline` reports the up-proj GEMM kernel
+(the headline shape) against the 5.0 POP/s dense int8 matrix peak, timed with
+HIP events on the stream the kernels run on.  `cpu_baseline` times the CPU
+oracle on a bounded row sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0       # MI355X dense int8 matrix peak, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, 8 TB/s
+METRIC = "fused W8A8 linear TOPS and % of MI355X INT8 MFMA peak, DiT shapes"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_mlp_up_m4096_k3072_n12288.json")
+GEMM_SRC = os.path.join(ROOT, "w8a8_int8_quantized_quantize_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--rotate", type=int, default=4, help="weight copies cycled across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle time")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every GEMM configuration on every workload shape instead")
+    ap.add_argument("--sweep-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+def gemm_src_hash() -> str:
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_entry():
+    """HBM bytes per launch of the up-proj GEMM from rocprofv3 counters, if
+    they were taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_src_sha256_16") != gemm_src_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def make_inputs(torch, w8, synthetic, rotate):
+    dev = "cuda:0"
+    up, down = synthetic.CONFIGS["dit1024_mlp"]
+    inp = {}
+
+    def lin(shape):
+        st = synthetic.streams(0, shape.config_id, shape.layer_id)
+        x = synthetic.activations_bf16(st, shape.M, shape.K, shape.outlier_frac).to(dev)
+        w = torch.from_numpy(synthetic.weights_f32(st, shape.N, shape.K)).to(dev)
+        b = synthetic.bias_bf16(st, shape.N).to(dev)
+        wq, sw = w8.w8a8_quantize_weight(w)
+        del w
+        copies = [(wq, sw)] + [(wq.clone(), sw.clone()) for _ in range(rotate - 1)]
+        return x, copies, b
+
+    inp["x_up"], inp["w_up"], inp["b_up"] = lin(up)
+    inp["r_down"], inp["w_down"], inp["b_down"] = lin(down)
+    M = up.M
+    inp["q_x"] = torch.empty((M, up.K), dtype=torch.int8, device=dev)
+    inp["s_x"] = torch.empty((M,), dtype=torch.float32, device=dev)
+    inp["y_up"] = torch.empty((M, up.N), dtype=torch.bfloat16, device=dev)
+    inp["q_h"] = torch.empty((M, down.K), dtype=torch.int8, device=dev)
+    inp["s_h"] = torch.empty((M,), dtype=torch.float32, device=dev)
+    inp["y_down"] = torch.empty((M, down.N), dtype=torch.bfloat16, device=dev)
+    return up, down, inp
+
+
+def cpu_baseline(up, down, seconds):
+    """The CPU oracle on rows 0..S-1 of the same step, S sized to ~`seconds`."""
+    import numpy as np
+
+    import oracle
+    import synthetic
+
+    def host_inputs(shape):
+        st = synthetic.streams(0, shape.config_id, shape.layer_id)
+        x = synthetic.bf16_bits(synthetic.activations_bf16(st, shape.M, shape.K, shape.outlier_frac))
+        w = synthetic.weights_f32(st, shape.N, shape.K)
+        b = synthetic.bf16_bits(synthetic.bias_bf16(st, shape.N))
+        return x, w, b
+
+    x, wu, bu = host_inputs(up)
+    r, wd, bd = host_inputs(down)
+    wuq, wus = oracle.quantize_rows_f32(wu)   # offline, untimed
+    wdq, wds = oracle.quantize_rows_f32(wd)
+
+    def step(S):
+        t0 = time.perf_counter()
+        oracle.linear(x[:S], wuq, wus, bu)
+        h = oracle.gelu_bf16(r[:S])
+        oracle.linear(h, wdq, wds, bd)
+        return time.perf_counter() - t0
+
+    S0 = 8
+    t = step(S0)
+    S = int(max(S0, min(up.M, S0 * seconds / max(t, 1e-6))))
+    t = step(S)
+    ops = 2.0 * S * (up.N * up.K + down.N * down.K)
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"rows 0..{S - 1} of the MLP step (per-token quantize + int64 GEMM + epilogue "
+                      f"for up-proj, fp64 GELU + quantize + GEMM + epilogue for down-proj), "
+                      f"{t:.1f} s wall, weights pre-quantized untimed",
+            "seconds": t}
+
+
+def sweep(args, torch, w8, synthetic):
+    dev = "cuda:0"
+    shapes = [s for v in synthetic.CONFIGS.values() for s in v]
+    for s in shapes:
+        q = torch.randint(-127, 128, (s.M, s.K), dtype=torch.int8, device=dev)
+        wq = torch.randint(-127, 128, (s.N, s.K), dtype=torch.int8, device=dev)
+        sx = torch.rand((s.M,), device=dev) * 0.01
+        sw = torch.rand((s.N,), device=dev) * 0.01
+        b = torch.randn((s.N,), device=dev).to(torch.bfloat16)
+        y = torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)
+        sel = w8.w8a8_gemm_select_config(s.M, s.N, s.K)
+        for c in range(w8.w8a8_gemm_num_configs()):
+            for _ in range(3):
+                w8.w8a8_gemm_ex(q, sx, wq, sw, b, out=y, config=c)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.sweep_iters + 1)]
+            evs[0].record()
+            for i in range(args.sweep_iters):
+                w8.w8a8_gemm_ex(q, sx, wq, sw, b, out=y, config=c)
+                evs[i + 1].record()
+            torch.cuda.synchronize()
+            ts = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.sweep_iters))
+            med = ts[len(ts) // 2]
+            tops = 2.0 * s.M * s.N * s.K / (med * 1e-3) / 1e12
+            gbs = (s.M * s.K + s.N * s.K + 2 * s.M * s.N + 6 * s.N) / (med * 1e-3) / 1e9
+            print(json.dumps({"sweep": s.name, "config": c, "name": w8.w8a8_gemm_config_name(c),
+                              "selected": c == sel, "us_median": round(med * 1e3, 2),
+                              "us_min": round(ts[0] * 1e3, 2), "TOPS": round(tops, 1),
+                              "GBs": round(gbs, 1)}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              f"(the layer shards over tokens or output channels without communication; see the "
+              f"design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synthetic
+    import w8a8_int8_quantized_quantize_amd as w8
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(args, torch, w8, synthetic)
+        return 0
+
+    up, down, inp = make_inputs(torch, w8, synthetic, args.rotate)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        wu, su = inp["w_up"][i % len(inp["w_up"])]
+        wd, sd = inp["w_down"][i % len(inp["w_down"])]
+        if ev is not None:
+            ev[0].record(stream)
+        w8.w8a8_quantize_act(inp["x_up"], inp["q_x"], inp["s_x"])
+        if ev is not None:
+            ev[1].record(stream)
+        w8.w8a8_gemm_dequant(inp["q_x"], inp["s_x"], wu, su, inp["b_up"], out=inp["y_up"])
+        if ev is not None:
+            ev[2].record(stream)
+        w8.w8a8_gelu_quantize_act(inp["r_down"], inp["q_h"], inp["s_h"])
+        if ev is not None:
+            ev[3].record(stream)
+        w8.w8a8_gemm_dequant(inp["q_h"], inp["s_h"], wd, sd, inp["b_down"], out=inp["y_down"])
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    seg = [[ev[j].elapsed_time(ev[j + 1]) for ev in events] for j in range(4)]
+    avg = [sum(s) / len(s) for s in seg]
+    ops_up = 2.0 * up.M * up.N * up.K
+    ops_down = 2.0 * down.M * down.N * down.K
+    value = (ops_up + ops_down) / (ms_step * 1e-3) / 1e12
+    gemm_up_tops = ops_up / (avg[1] * 1e-3) / 1e12
+    gemm_down_tops = ops_down / (avg[3] * 1e-3) / 1e12
+    q_bytes = 3.0 * up.M * up.K + 4 * up.M
+    g_bytes = 3.0 * down.M * down.K + 4 * down.M
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "dit1024_mlp: 4096 tokens; up-proj K=3072 N=12288; "
+                               "GELU+requantize; down-proj K=12288 N=3072",
+                   "M": up.M, "hidden": up.K, "mlp": up.N, "weight_copies_rotated": args.rotate},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_up_tops, 1), "peak": PEAK_INT8_TOPS,
+                     "unit": "TOP/s", "frac": round(gemm_up_tops / PEAK_INT8_TOPS, 4),
+                     "traffic": traffic_entry(),
+                     "kernel": "gemm_kernel, up-proj M=4096 K=3072 N=12288 (int8 ops per launch "
+                               "2*M*N*K / mean HIP-event duration)"},
+        "kernels_ms": {"quantize_x": round(avg[0], 4), "gemm_up": round(avg[1], 4),
+                       "gelu_quantize_r": round(avg[2], 4), "gemm_down": round(avg[3], 4)},
+        "per_kernel": {
+            "gemm_up_TOPS": round(gemm_up_tops, 1), "gemm_down_TOPS": round(gemm_down_tops, 1),
+            "quantize_x_GBs": round(q_bytes / (avg[0] * 1e-3) / 1e9, 1),
+            "gelu_quantize_GBs": round(g_bytes / (avg[2] * 1e-3) / 1e9, 1),
+            "gemm_up_config": w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(up.M, up.N, up.K)),
+            "gemm_down_config": w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(down.M, down.N, down.K)),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(up, down, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,173 @@
+/*
+ * w8a8.h -- C ABI of libw8a8.so, a W8A8 INT8 linear layer for AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * The operation is the fused INT8 linear of "Realizing Native INT8 Compute for
+ * Diffusion Transformers on Consumer GPUs: A Fused INT8 GEMM Kernel for
+ * Ideogram 4.0" (Asaria, Salomone, Gandhi; arXiv 2606.14598), Abstract:
+ * activations are quantized to int8 per token and weights per output channel
+ * (post-training), the int8 x int8 products are accumulated in int32 on the
+ * integer matrix units, and the per-token x per-channel dequantization and the
+ * bias are applied in the GEMM epilogue.  The Spanish write-up of the same
+ * paper (aiexpert.news, "Núcleo Tritón Fuso Reduce el Tiempo de Generación de
+ * Imágenes en 9,5% en Ampere de Consumo", second paragraph) adds that the
+ * epilogue emits bf16 directly, without an extra round trip through memory.
+ *
+ * Numerical contract (the pages leave these open; this library fixes them):
+ *   scale  = fl32(absmax_of_row / 127)                       (IEEE division)
+ *   code   = clamp(round_half_even(fl32(x / scale)), -127, 127); scale 0 -> 0
+ *   acc    = sum_k code_x[m,k] * code_w[n,k]                  (exact, int32)
+ *   y      = bf16_rne( fl32( fl32( fl32(s_x[m]*s_w[n]) * fl32(acc) ) + bias[n] ) )
+ *            -- every step one IEEE fp32 operation, no fused multiply-add.
+ *
+ * Conventions for every entry point below:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing and keeps no mutable state; calls are thread-safe.
+ *   - Matrices are row-major with the reduction dimension K contiguous.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Work is enqueued asynchronously on it; the return value covers argument
+ *     validation and launch errors only.
+ *   - Sizes: M, N >= 0 and 0 <= K <= W8A8_MAX_K with K % 16 == 0.  A call with
+ *     nothing to compute returns W8A8_OK and enqueues nothing.  Pointers to
+ *     tensors with zero elements may be NULL.
+ *   - Alignment: int8 / bf16 / int32 matrix pointers 16-byte aligned; leading
+ *     dimensions (in elements) such that every row starts 16-byte aligned;
+ *     fp32 scale vectors 4-byte aligned, bf16 bias 2-byte aligned.
+ *   - On any status other than W8A8_OK nothing has been enqueued (for
+ *     W8A8_ERR_HIP: the launch itself failed).
+ *   - Non-finite inputs are outside the contract: outputs are then
+ *     unspecified, but every access stays in bounds.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest K for which |acc| <= 127*127*K cannot overflow int32, rounded down
+ * to a multiple of 16:  16129 * 133136 = 2147350544 <= 2^31 - 1. */
+#define W8A8_MAX_K 133136
+
+enum w8a8_status {
+  W8A8_OK = 0,
+  W8A8_ERR_NULL = 1,       /* a required pointer is NULL */
+  W8A8_ERR_SHAPE = 2,      /* negative size, K % 16 != 0, or ld < K */
+  W8A8_ERR_ALIGN = 3,      /* pointer or row stride not aligned as above */
+  W8A8_ERR_K_OVERFLOW = 4, /* K > W8A8_MAX_K: int32 accumulation could overflow */
+  W8A8_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required */
+  W8A8_ERR_HIP = 6,        /* the HIP runtime rejected a launch */
+  W8A8_ERR_CONFIG = 7      /* unknown GEMM kernel configuration id */
+};
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* w8a8_status_string(int status);
+
+/*
+ * Per-token activation quantization.
+ *   x      bf16 [M, K], row stride ldx elements (ldx >= K, ldx % 8 == 0)
+ *   q      int8 [M, K] out, row stride ldq (ldq >= K, ldq % 16 == 0)
+ *   scale  fp32 [M] out: scale[m] = absmax(x[m, :]) / 127
+ * Source: the Abstract's per-token activation quantization.
+ */
+int w8a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                      int8_t* q, int64_t ldq, float* scale, void* stream);
+
+/*
+ * Per-output-channel weight quantization (run once, offline), same rule on
+ * fp32 rows.
+ *   w      fp32 [N, K], row stride ldw (ldw >= K, ldw % 4 == 0)
+ *   q      int8 [N, K] out, row stride ldq (ldq >= K, ldq % 16 == 0)
+ *   scale  fp32 [N] out
+ * Source: the Abstract's per-channel weight quantization; the news write-up
+ * (second-to-last paragraph of its body) says it is done after training.
+ */
+int w8a8_quantize_weight(const float* w, int64_t N, int64_t K, int64_t ldw,
+                         int8_t* q, int64_t ldq, float* scale, void* stream);
+
+/*
+ * Debug entry: the int32 accumulators alone, written to memory.
+ *   q_x  int8 [M, K] (row stride K), w_q int8 [N, K] (row stride K)
+ *   acc  int32 [M, N] out (row stride N): acc[m,n] = sum_k q_x[m,k] * w_q[n,k]
+ * Source: the Abstract's int8 x int8 -> int32 accumulation, which the paper
+ * checks bit for bit against a reference integer matmul.
+ */
+int w8a8_gemm_i32(const int8_t* q_x, const int8_t* w_q, int64_t M, int64_t N, int64_t K,
+                  int32_t* acc, void* stream);
+
+/*
+ * int8 GEMM with the fused dequantization + bias epilogue, on activations
+ * that are already quantized (e.g. by w8a8_gelu_quantize_act).
+ *   q_x  int8 [M, K], s_x fp32 [M], w_q int8 [N, K], s_w fp32 [N]
+ *   bias bf16 [N] or NULL (no bias)
+ *   y    bf16 [M, N] out (row stride N)
+ * The int32 accumulators never leave registers.
+ * Source: the Abstract's epilogue folding of dequantization and bias.
+ */
+int w8a8_gemm_dequant(const int8_t* q_x, const float* s_x, const int8_t* w_q,
+                      const float* s_w, const void* bias_bf16, int64_t M, int64_t N,
+                      int64_t K, void* y_bf16, void* stream);
+
+/* Bytes of device workspace w8a8_linear needs: the int8 codes [M, K] and the
+ * fp32 scales [M] of the activations, each padded to 256 bytes. */
+size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
+
+/*
+ * The fused W8A8 linear: per-token quantization of x into the workspace, then
+ * the int8 GEMM with the dequantization + bias epilogue.
+ *   x     bf16 [M, K] (row stride K)
+ *   w_q   int8 [N, K], s_w fp32 [N]   (from w8a8_quantize_weight)
+ *   bias  bf16 [N] or NULL
+ *   y     bf16 [M, N] out
+ *   workspace  device memory of at least w8a8_linear_workspace_bytes(M, K),
+ *              16-byte aligned; its contents on return are the codes and
+ *              scales of x.  Calls sharing one workspace must be ordered.
+ * Source: the Abstract's fused INT8 GEMM that replaces the
+ * dequantize-to-bf16 linear forward.
+ */
+int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w,
+                const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * GELU followed by per-token quantization, for the activation between the
+ * two linears of a DiT MLP (not on the pages; part of the DiT MLP workload):
+ *   h[m,k] = bf16_rne(gelu(y[m,k])),  gelu(v) = 0.5 * v * erfc(-v / sqrt(2))
+ *   then q, scale from h exactly as w8a8_quantize_act.
+ *   y      bf16 [M, K], row stride ldy (ldy >= K, ldy % 8 == 0)
+ *   q      int8 [M, K] out (row stride ldq), scale fp32 [M] out
+ *   h_out  bf16 [M, K] out (row stride K) or NULL: the GELU values that were
+ *          quantized, for inspection.
+ */
+int w8a8_gelu_quantize_act(const void* y_bf16, int64_t M, int64_t K, int64_t ldy,
+                           int8_t* q, int64_t ldq, float* scale, void* h_out_bf16,
+                           void* stream);
+
+/*
+ * GEMM kernel configurations (tile shapes), chosen per GEMM shape -- the
+ * Abstract's per-shape autotuning, here a fixed table built from measurement.
+ */
+int w8a8_gemm_num_configs(void);
+/* Name of configuration `config` (static storage), or NULL if out of range. */
+const char* w8a8_gemm_config_name(int config);
+/* The configuration the library uses for an (M, N, K) GEMM. */
+int w8a8_gemm_select_config(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w8a8_gemm_i32 / w8a8_gemm_dequant with an explicit configuration
+ * (config = -1: the library's choice).  out_int32 != 0 writes int32
+ * accumulators to `out` (s_x, s_w, bias ignored); otherwise bf16 as
+ * w8a8_gemm_dequant.  Every configuration computes the same bits.
+ */
+int w8a8_gemm_ex(const int8_t* q_x, const float* s_x, const int8_t* w_q, const float* s_w,
+                 const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* out,
+                 int out_int32, int config, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

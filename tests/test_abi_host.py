@@ -1,0 +1,121 @@
+"""Host-side tests of the C-ABI library: it loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+any HIP call (so these run on a machine without a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import subprocess
+
+import pytest
+
+import w8a8_int8_quantized_quantize_amd as w8
+
+L = w8.raw()
+P = ctypes.c_void_p
+A = P(0x10000)      # a fake, 16-byte aligned address: never dereferenced, as
+MIS = P(0x10001)    # every call below fails validation before any launch
+
+OK, NULL, SHAPE, ALIGN, KOVF, WS, HIP, CFG = range(8)
+
+
+def test_exports_every_declared_function():
+    names = w8.header_functions()
+    assert len(names) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", w8.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert getattr(L, n) is not None
+
+
+def test_status_strings():
+    for s in range(8):
+        assert w8.w8a8_status_string(s).startswith("W8A8_")
+    assert "unknown" in w8.w8a8_status_string(123)
+
+
+def test_quantize_validation():
+    q = L.w8a8_quantize_act
+    assert q(None, 0, 16, 16, None, 16, None, None) == OK          # nothing to do
+    assert q(None, -1, 16, 16, None, 16, None, None) == SHAPE
+    assert q(A, 4, 17, 17, A, 32, A, None) == SHAPE                 # K % 16
+    assert q(A, 4, 32, 16, A, 32, A, None) == SHAPE                 # ldx < K
+    assert q(A, 4, 32, 32, A, 16, A, None) == SHAPE                 # ldq < K
+    assert q(None, 4, 16, 16, A, 16, A, None) == NULL
+    assert q(A, 4, 16, 16, None, 16, A, None) == NULL
+    assert q(A, 4, 16, 16, A, 16, None, None) == NULL
+    assert q(MIS, 4, 16, 16, A, 16, A, None) == ALIGN
+    assert q(A, 4, 16, 16, MIS, 16, A, None) == ALIGN
+    assert q(A, 4, 16, 20, A, 16, A, None) == ALIGN                 # bf16 row stride 40 B
+    assert q(A, 4, 16, 16, A, 24, A, None) == ALIGN                 # int8 row stride 24 B
+    assert q(A, 4, 16, 16, A, 16, P(0x10002), None) == ALIGN        # fp32 scale
+    assert q(A, 4, 133152, 133152, A, 133152, A, None) == KOVF
+    w = L.w8a8_quantize_weight
+    assert w(A, 4, 16, 18, A, 16, A, None) == ALIGN                 # fp32 row stride 72 B
+    assert w(A, 4, 16, 16, A, 16, None, None) == NULL
+    g = L.w8a8_gelu_quantize_act
+    assert g(A, 4, 16, 16, A, 16, A, MIS, None) == ALIGN
+    assert g(A, 4, 15, 16, A, 16, A, None, None) == SHAPE
+
+
+def test_gemm_validation():
+    g = L.w8a8_gemm_i32
+    assert g(None, None, 0, 5, 16, None, None) == OK
+    assert g(None, None, 5, 0, 16, None, None) == OK
+    assert g(A, A, -1, 4, 16, A, None) == SHAPE
+    assert g(A, A, 4, 4, 8, A, None) == SHAPE
+    assert g(A, A, 4, 4, 133152, A, None) == KOVF
+    assert g(A, A, 4, 4, 16, None, None) == NULL
+    assert g(None, A, 4, 4, 16, A, None) == NULL
+    assert g(A, MIS, 4, 4, 16, A, None) == ALIGN
+    d = L.w8a8_gemm_dequant
+    assert d(A, None, A, A, None, 4, 4, 16, A, None) == NULL        # s_x
+    assert d(A, A, A, None, None, 4, 4, 16, A, None) == NULL        # s_w
+    assert d(A, P(0x10002), A, A, None, 4, 4, 16, A, None) == ALIGN
+    assert d(A, A, A, A, P(0x10001), 4, 4, 16, A, None) == ALIGN    # bias
+    e = L.w8a8_gemm_ex
+    assert e(A, A, A, A, None, 4, 4, 16, A, 0, 99, None) == CFG
+    assert e(A, A, A, A, None, 4, 4, 16, A, 0, -2, None) == CFG
+    assert e(A, A, A, A, None, 4, 4, 16, A, 1, w8.w8a8_gemm_num_configs(), None) == CFG
+
+
+def test_linear_validation_and_workspace():
+    ws = w8.w8a8_linear_workspace_bytes
+    assert ws(0, 16) == 0
+    assert ws(1, 16) == 256 + 256
+    assert ws(4096, 3072) == 4096 * 3072 + 4096 * 4
+    assert ws(3, 48) == 256 + 256
+    assert ws(300, 1040) == (300 * 1040 + 255) // 256 * 256 + (1200 + 255) // 256 * 256
+    lin = L.w8a8_linear
+    need = ws(4, 16)
+    assert lin(A, A, A, None, 4, 4, 16, A, None, need, None) == WS
+    assert lin(A, A, A, None, 4, 4, 16, A, A, need - 1, None) == WS
+    assert lin(A, A, A, None, 4, 4, 16, A, MIS, need, None) == ALIGN
+    assert lin(A, A, A, None, 4, 4, 17, A, A, need, None) == SHAPE
+    assert lin(A, A, A, None, 4, 4, 133152, A, A, 1 << 40, None) == KOVF
+    assert lin(None, A, A, None, 4, 4, 16, A, A, need, None) == NULL
+    assert lin(A, A, None, None, 4, 4, 16, A, A, need, None) == NULL
+    assert lin(None, None, None, None, 0, 4, 16, None, None, 0, None) == OK
+
+
+def test_config_selection_table():
+    n = w8.w8a8_gemm_num_configs()
+    names = [w8.w8a8_gemm_config_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert w8.w8a8_gemm_config_name(n) is None and w8.w8a8_gemm_config_name(-1) is None
+    import synthetic
+    for shapes in synthetic.CONFIGS.values():
+        for s in shapes:
+            c = w8.w8a8_gemm_select_config(s.M, s.N, s.K)
+            assert 0 <= c < n, s
+    assert w8.w8a8_gemm_select_config(0, 4, 16) == -1
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 16), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        w8.w8a8_quantize_act(x)
+    with pytest.raises(TypeError):
+        w8.w8a8_gemm_i32(torch.zeros((4, 16), dtype=torch.int8), torch.zeros((4, 16), dtype=torch.int8))

@@ -1,0 +1,313 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: int8 codes, fp32 scales and int32 accumulators bit-exact; bf16 outputs
+within 1 ulp (both sides use the same fp32 operation order, so they are
+expected to be bit-exact and the count of non-identical elements is checked
+to be zero as well), cosine >= 0.99999, no NaN/Inf.
+
+Small and mid sizes are compared element by element over the whole output;
+they span several tiles of every kernel configuration with ragged M, N and K
+tails.  The full workload sizes are compared on sampled rows (rows are
+independent in this layer, so the oracle computes a row subset exactly) plus
+whole-output checks that hold at any size.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+import w8a8_int8_quantized_quantize_amd as w8
+from gpu_helpers import (DEV, assert_bf16_parity, bits, dev_bf16, host, sample_rows,
+                         shape_inputs, ulp_dist)
+
+pytestmark = pytest.mark.gpu
+
+NCFG = None
+
+
+def ncfg():
+    global NCFG
+    if NCFG is None:
+        NCFG = w8.w8a8_gemm_num_configs()
+    return NCFG
+
+
+def rand_bits(rng, M, K, scale=1.0, outliers=0):
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.float32(scale)
+    if outliers:
+        x[:, rng.permutation(K)[:outliers]] *= np.float32(20.0)
+    return synthetic.bf16_bits(synthetic.bf16_from_f32(x))
+
+
+# ------------------------------------------------------------ quantization --
+QSHAPES = [(1, 16), (7, 48), (33, 1040), (64, 256), (257, 3072), (5, 12288), (3, 16384),
+           (2, 24592), (1, 133136)]
+
+
+@pytest.mark.parametrize("M,K", QSHAPES)
+def test_quantize_act_bit_exact(M, K):
+    rng = np.random.default_rng(M * 7919 + K)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    if M > 2:
+        xb[1] = 0                                    # all-zero row
+        xb[2] = rand_bits(rng, 1, K, scale=1e-39)[0]  # subnormal-range row
+    q, s = w8.w8a8_quantize_act(dev_bf16(xb))
+    qo, so = oracle.quantize_rows_bf16(xb)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+def test_quantize_act_ties_and_strided_rows():
+    # rows with absmax 127 (scale 1) and exact .5 ties; a row stride > K
+    vals = np.array([127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, 3.5, -3.5, 0, -127, 63.5, 64.5, 1, 2],
+                    np.float32)
+    xb = synthetic.bf16_bits(synthetic.bf16_from_f32(np.tile(vals, (3, 4))))
+    big = np.zeros((3, 128), np.uint16)
+    big[:, :64] = xb
+    xt = dev_bf16(big)[:, :64]
+    q, s = w8.w8a8_quantize_act(xt)
+    qo, so = oracle.quantize_rows_bf16(xb)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    assert host(q)[0, :16].tolist() == [127, 0, 2, 2, 0, -2, -2, 126, 4, -4, 0, -127, 64, 64, 1, 2]
+
+
+@pytest.mark.parametrize("N,K", [(128, 256), (300, 1040), (64, 12288), (3, 16)])
+def test_quantize_weight_bit_exact(N, K):
+    rng = np.random.default_rng(N + K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if N > 2:
+        w[1] = 0
+        w[2] = np.float32(2.0 ** -149) * rng.integers(-200, 200, K).astype(np.float32)
+    q, s = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    qo, so = oracle.quantize_rows_f32(w)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (2, 16384), (4, 48)])
+def test_gelu_quantize_teacher_forced(M, K):
+    rng = np.random.default_rng(M + 3 * K)
+    yb = rand_bits(rng, M, K, scale=3.0, outliers=max(1, K // 100))
+    q, s, h = w8.w8a8_gelu_quantize_act(dev_bf16(yb), want_h=True)
+    ho = oracle.gelu_bf16(yb)
+    hg = bits(h)
+    d = ulp_dist(hg, ho)
+    assert d.max() <= 1
+    assert np.mean(d == 0) > 0.999
+    # codes and scales: bit-exact against the oracle's quantization of the
+    # GPU's own GELU values (a 1-ulp GELU difference at a row's absmax would
+    # otherwise move that row's scale)
+    qo, so = oracle.quantize_rows_bf16(hg)
+    assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
+    # without the debug copy the codes are the same
+    q2, s2, _ = w8.w8a8_gelu_quantize_act(dev_bf16(yb))
+    assert torch.equal(q2, q) and torch.equal(s2, s)
+
+
+# -------------------------------------------------------------------- GEMM --
+GSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
+           (257, 16, 16), (16, 1000, 3072), (129, 257, 144)]
+
+
+@pytest.mark.parametrize("M,N,K", GSHAPES)
+def test_gemm_i32_bit_exact_every_config(M, N, K):
+    rng = np.random.default_rng(M * 31 + N * 7 + K)
+    a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    want = oracle.gemm_i64(a, b)
+    qa, qb = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    got = host(w8.w8a8_gemm_i32(qa, qb))
+    assert np.array_equal(got.astype(np.int64), want)
+    for c in range(ncfg()):
+        g = host(w8.w8a8_gemm_ex(qa, None, qb, None, out_int32=True, config=c))
+        assert np.array_equal(g.astype(np.int64), want), w8.w8a8_gemm_config_name(c)
+
+
+def test_gemm_i32_extremes_at_max_k():
+    K = w8.W8A8_MAX_K
+    a = np.full((17, K), 127, np.int8)
+    a[1::2] = -127
+    b = np.full((18, K), 127, np.int8)
+    b[::3] = -127
+    got = host(w8.w8a8_gemm_i32(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)))
+    want = oracle.gemm_i64(a, b)
+    assert np.abs(want).max() == 16129 * K
+    assert np.array_equal(got.astype(np.int64), want)
+
+
+@pytest.mark.parametrize("M,N,K", GSHAPES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_linear_bf16_parity_every_config(M, N, K, with_bias):
+    rng = np.random.default_rng(M + N + K + with_bias)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0] if with_bias else None
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    wqo, swo = oracle.quantize_rows_f32(w)
+    assert np.array_equal(host(wq), wqo) and np.array_equal(host(sw), swo)
+    want = oracle.linear(xb, wqo, swo, bb)
+    x = dev_bf16(xb)
+    bias = dev_bf16(bb) if with_bias else None
+    y = w8.w8a8_linear(x, wq, sw, bias)
+    n_diff = assert_bf16_parity(bits(y), want["y"], f"linear {M}x{N}x{K}")
+    assert n_diff == 0
+    q, s = w8.w8a8_quantize_act(x)
+    for c in range(ncfg()):
+        yc = w8.w8a8_gemm_ex(q, s, wq, sw, bias, config=c)
+        assert np.array_equal(bits(yc), want["y"]), w8.w8a8_gemm_config_name(c)
+
+
+def test_linear_k_zero_is_bias_and_empty_batches():
+    N = 40
+    rng = np.random.default_rng(5)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0]
+    wq = torch.zeros((N, 0), dtype=torch.int8, device=DEV)
+    sw = torch.ones((N,), dtype=torch.float32, device=DEV)
+    x = torch.zeros((3, 0), dtype=torch.bfloat16, device=DEV)
+    y = w8.w8a8_linear(x, wq, sw, dev_bf16(bb))
+    assert np.array_equal(bits(y), np.tile(bb, (3, 1)))
+    y0 = w8.w8a8_linear(x, wq, sw)  # no bias: (s_x * s_w) * 0 = +0
+    assert np.all(bits(y0) == 0)
+    # M = 0 and N = 0
+    e = w8.w8a8_linear(torch.zeros((0, 32), dtype=torch.bfloat16, device=DEV),
+                       torch.zeros((N, 32), dtype=torch.int8, device=DEV), sw)
+    assert e.shape == (0, N)
+    e2 = w8.w8a8_gemm_i32(torch.zeros((5, 32), dtype=torch.int8, device=DEV),
+                          torch.zeros((0, 32), dtype=torch.int8, device=DEV))
+    assert e2.shape == (5, 0)
+    q, s = w8.w8a8_quantize_act(torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV))
+    assert q.shape == (0, 64) and s.shape == (0,)
+
+
+def test_deterministic_and_stream_ordered():
+    rng = np.random.default_rng(11)
+    M, N, K = 300, 520, 1040
+    x = dev_bf16(rand_bits(rng, M, K))
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(DEV))
+    ref = w8.w8a8_linear(x, wq, sw)
+    s = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(s):
+        outs = [w8.w8a8_linear(x, wq, sw) for _ in range(3)]
+    s.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))
+
+
+def test_int_mm_cross_check_where_available():
+    # The pages check the int32 accumulators against torch._int_mm; do the same
+    # where this PyTorch build provides it on the device.
+    rng = np.random.default_rng(12)
+    M, N, K = 64, 128, 256
+    a = torch.from_numpy(rng.integers(-127, 128, (M, K)).astype(np.int8)).to(DEV)
+    b = torch.from_numpy(rng.integers(-127, 128, (N, K)).astype(np.int8)).to(DEV)
+    try:
+        ref = torch._int_mm(a, b.t().contiguous())
+    except Exception as e:  # not supported on this build / shape
+        pytest.skip(f"torch._int_mm unavailable: {e}")
+    assert torch.equal(w8.w8a8_gemm_i32(a, b), ref)
+
+
+# ---------------------------------------------------- full workload sizes --
+def _full_linear_check(shape, x_bits, n_rows=24):
+    """Run the fused linear at full size on the GPU; compare sampled rows."""
+    _, w, b = shape_inputs(shape)
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    wqo, swo = oracle.quantize_rows_f32(w)
+    assert np.array_equal(host(wq), wqo) and np.array_equal(host(sw), swo)
+    x = dev_bf16(x_bits)
+    y = w8.w8a8_linear(x, wq, sw, dev_bf16(b))
+    q, s = w8.w8a8_quantize_act(x)
+    qo, so = oracle.quantize_rows_bf16(x_bits)          # whole activation tensor
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    yb = bits(y)
+    assert ((yb & 0x7F80) != 0x7F80).all()              # no NaN/Inf anywhere
+    rows = sample_rows(shape.M, n_rows)
+    want = oracle.linear_prequant(qo[rows], so[rows], wqo, swo, b)
+    assert np.abs(want["acc"]).max() <= 16129 * shape.K
+    n_diff = assert_bf16_parity(yb[rows], want["y"], shape.name)
+    assert n_diff == 0
+    return yb
+
+
+FULL = [s for k in ("unit", "dit768_attn", "skinny") for s in synthetic.CONFIGS[k]] + \
+       [synthetic.CONFIGS["dit1024_mlp"][0]]
+
+
+@pytest.mark.parametrize("shape", FULL, ids=lambda s: s.name)
+def test_full_size_linear_sampled(shape):
+    x, _, _ = shape_inputs(shape)
+    _full_linear_check(shape, x)
+
+
+def test_full_size_mlp_down_with_gelu_input():
+    # down-proj input: GELU of a random bf16 tensor with outlier columns
+    shape = synthetic.CONFIGS["dit1024_mlp"][1]
+    r, _, _ = shape_inputs(shape)
+    q, s, h = w8.w8a8_gelu_quantize_act(dev_bf16(r), want_h=True)
+    hb = bits(h)
+    rows = sample_rows(shape.M, 64)
+    assert ulp_dist(hb[rows], oracle.gelu_bf16(r[rows])).max() <= 1
+    qo, so = oracle.quantize_rows_bf16(hb)
+    assert np.array_equal(host(q), qo) and np.array_equal(host(s), so)
+    _, w, b = shape_inputs(shape)
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    y = bits(w8.w8a8_gemm_dequant(q, s, wq, sw, dev_bf16(b)))
+    assert ((y & 0x7F80) != 0x7F80).all()
+    wqo, swo = oracle.quantize_rows_f32(w)
+    want = oracle.linear_prequant(qo[rows], so[rows], wqo, swo, b)
+    assert assert_bf16_parity(y[rows], want["y"], shape.name) == 0
+
+
+def test_full_size_dit_block_chain():
+    """QKV -> out-proj (random stand-in for attention) -> up -> GELU -> down,
+    re-quantizing per token between layers.  Each stage teacher-forced on the
+    GPU's own input; the whole chain also against an un-forced oracle chain on
+    sampled rows (rows are independent through the whole chain)."""
+    qkv, out, up, down = synthetic.CONFIGS["dit1024_chain"]
+    M = qkv.M
+    rows = sample_rows(M, 16)
+    layers = {}
+    for s in (qkv, out, up, down):
+        _, w, b = shape_inputs(s)
+        wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+        layers[s.name] = (wq, sw, dev_bf16(b), oracle.quantize_rows_f32(w), b)
+    x0, _, _ = shape_inputs(qkv)
+    a_bits, _, _ = shape_inputs(synthetic.GemmShape("attn_standin", M, 3072, 3072, 0.0, 5, 9))
+
+    def run(s, xb_dev):
+        wq, sw, bd, _, _ = layers[s.name]
+        return w8.w8a8_linear(xb_dev, wq, sw, bd)
+
+    def oracle_rows(s, x_rows_bits):
+        _, _, _, (wqo, swo), b = layers[s.name]
+        return oracle.linear(x_rows_bits, wqo, swo, b)["y"]
+
+    y_qkv = bits(run(qkv, dev_bf16(x0)))
+    assert assert_bf16_parity(y_qkv[rows], oracle_rows(qkv, x0[rows]), "qkv") == 0
+    y1 = run(out, dev_bf16(a_bits))
+    y1b = bits(y1)
+    assert assert_bf16_parity(y1b[rows], oracle_rows(out, a_bits[rows]), "out") == 0
+    y2 = run(up, y1)
+    y2b = bits(y2)
+    assert assert_bf16_parity(y2b[rows], oracle_rows(up, y1b[rows]), "up") == 0
+    qh, sh, h = w8.w8a8_gelu_quantize_act(y2, want_h=True)
+    hb = bits(h)
+    assert ulp_dist(hb[rows], oracle.gelu_bf16(y2b[rows])).max() <= 1
+    qo, so = oracle.quantize_rows_bf16(hb[rows])
+    assert np.array_equal(host(qh)[rows], qo) and np.array_equal(host(sh)[rows], so)
+    wq, sw, bd, (wqo, swo), b = layers[down.name]
+    y3 = bits(w8.w8a8_gemm_dequant(qh, sh, wq, sw, bd))
+    assert ((y3 & 0x7F80) != 0x7F80).all()
+    want3 = oracle.linear_prequant(qo, so, wqo, swo, b)["y"]
+    assert assert_bf16_parity(y3[rows], want3, "down") == 0
+    # un-forced oracle chain on the sampled rows: information plus a loose bar
+    c1 = oracle_rows(out, a_bits[rows])
+    c2 = oracle_rows(up, c1)
+    ch = oracle.gelu_bf16(c2)
+    qo2, so2 = oracle.quantize_rows_bf16(ch)
+    c3 = oracle.linear_prequant(qo2, so2, wqo, swo, b)["y"]
+    from gpu_helpers import cosine
+    assert cosine(y3[rows], c3) >= 0.9999

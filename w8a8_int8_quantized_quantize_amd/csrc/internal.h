@@ -1,0 +1,38 @@
+// Internal declarations shared by the HIP translation units of libw8a8.so.
+// Not part of the public ABI (that is include/w8a8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// ---------------------------------------------------------- quantization --
+// Row-wise symmetric int8 quantization of bf16 (per token) or fp32 (per
+// channel) rows, optionally with GELU applied to bf16 rows first.  All sizes
+// already validated by the API layer; M >= 1.
+enum class QuantSrc { kBf16, kF32, kBf16Gelu };
+
+hipError_t launch_quantize_rows(QuantSrc src, const void* x, int64_t M, int64_t K, int64_t ldx,
+                                int8_t* q, int64_t ldq, float* scale, uint16_t* h_out,
+                                hipStream_t stream);
+
+// ------------------------------------------------------------------ GEMM --
+struct GemmArgs {
+  const int8_t* qx;   // [M, K] activations (codes), row stride K
+  const int8_t* qw;   // [N, K] weights (codes), row stride K
+  const float* sx;    // [M] per-token scales (bf16 output only)
+  const float* sw;    // [N] per-channel scales (bf16 output only)
+  const uint16_t* bias;  // [N] bf16 or nullptr
+  void* out;          // [M, N] bf16 or int32
+  int64_t M, N, K;
+};
+
+int gemm_num_configs();
+const char* gemm_config_name(int cfg);
+int gemm_select_config(int64_t M, int64_t N, int64_t K);
+// out_int32: write raw accumulators instead of the dequantized bf16.
+hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t stream);
+
+}  // namespace w8a8
