@@ -7,60 +7,110 @@
 // paper's kernel targets Ampere tensor cores; this one is designed for CDNA4:
 //
 //  * MFMA v_mfma_i32_16x16x64_i8.  The weight tile is the MFMA "A" operand and
-//    the activation tile the "B" operand, so the 16x16 result block holds
+//    the activation tile the "B" operand, so a 16x16 result block holds
 //    D[n][m]: each lane owns four consecutive output columns n of one row m,
 //    which the epilogue writes as one 8-byte bf16 store (16 bytes for int32).
-//  * Both operands are K-contiguous ([M,K] and [N,K] row-major), which is
-//    exactly what the MFMA operand layout wants: every lane reads 16
-//    consecutive k of one row with a single ds_read_b128, no transposes.
-//  * LDS: BK = 128 bytes of K per stage, double buffered.  Each tile row is
-//    128 B; its eight 16-byte chunks are XOR-swizzled by the row index so that
-//    both the global->LDS writes (8 lanes per row) and the MFMA operand reads
-//    (16 rows at one chunk) hit distinct banks.
-//  * Global loads are 16 B per lane, 8 lanes covering one 128-byte row segment.
+//  * Both operands are K-contiguous ([M,K] and [N,K] row-major), which is what
+//    the MFMA operand layout wants: every lane reads 16 consecutive k of one
+//    row with a single ds_read_b128, no transposes anywhere.
+//  * Global -> LDS with global_load_lds_dwordx4: each wave instruction moves
+//    1 KiB straight into LDS (lane i fills bytes 16i..16i+15 of the block), so
+//    no staging registers and no ds_write instructions.  The XOR swizzle of
+//    the 16-byte chunks inside a row is applied on the global side: a lane
+//    loads the logical chunk that belongs in its fixed LDS slot.
+//  * LDS pipeline of STAGES buffers of BK bytes of K; waits use explicit
+//    vmcnt counts so later stages stay in flight, and raw s_barrier.
+//  * Persistent workgroups walk the tile list; the next tile's first stages
+//    are issued before the current tile's epilogue, so their latency hides
+//    behind the epilogue's arithmetic and stores.
 //  * Tile order: the dispatcher deals workgroups round-robin to the 8 XCDs,
-//    each with its own L2.  Tile ids are remapped so that each XCD receives a
-//    contiguous range, walked in groups of 8 M-tiles ("grouped" order), so the
-//    workgroups sharing an L2 also share activation and weight panels.
+//    each with its own L2.  Tile ids are remapped so each XCD receives a
+//    contiguous range, walked in groups of 8 M-tiles, so the workgroups
+//    sharing an L2 also share activation and weight panels.
 //  * Epilogue in fp32, no contraction: (s_x[m] * s_w[n]) * float(acc) + bias[n],
 //    rounded once to bf16 (v_cvt_pk_bf16_f32, round to nearest even).  The
 //    int32 accumulators never touch memory unless the int32 debug output is
 //    requested.
 //
-// Ragged edges: rows beyond M / N and chunks beyond K are zero-filled in LDS;
-// out-of-range outputs are never stored.  K is a multiple of 16 (API contract),
-// so a 16-byte chunk is either entirely inside K or entirely outside.
+// Ragged edges: operand rows beyond M / N are clamped to the last row (their
+// results are never stored); 16-byte chunks beyond K are clamped in address
+// and zeroed in the activation fragment before the MFMA.  K is a multiple of
+// 16 (API contract), so a chunk is entirely inside or outside K.
 #include "internal.h"
 
 namespace w8a8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kGroupM = 8;  // M-tiles per group in the grouped tile order
 
-// XOR swizzle of the 16-byte chunk index inside a 128-byte LDS row.  Rows r and
-// r+8 differ as well, so 16 consecutive rows read at one logical chunk land in
-// 16 distinct bank groups even when two rows share a 256-byte bank line.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row ^ (row >> 3)) & 7);
+// Swizzled slot of logical 16-byte chunk c in LDS row r.  The pattern
+// depends on r & 15 only, so every fragment of a tile shares it and fragment
+// addresses differ by compile-time offsets.  128-byte rows (8 chunks): any 8
+// aligned consecutive rows read at one chunk hit 8 distinct 16-byte bank
+// groups, and any 16 rows hit 16 distinct (row parity, slot) pairs, i.e. no
+// conflict whether a 256-byte bank line holds one or two rows.  64-byte rows
+// (4 chunks): the same for 2 and 4 rows per bank line.
+template <int SLOTS>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (SLOTS == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
+  else return c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
-template <int BM_, int BN_, int WM_, int WN_>
+// MFMA shapes.  MF = 32: v_mfma_i32_32x32x32_i8, 32 bytes of K per step; lane
+// l holds row l % 32 of a 32-row fragment, K bytes 16 (l / 32) .. +15, and the
+// result D[i][j] sits in lane j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8).
+// MF = 16: v_mfma_i32_16x16x64_i8, 64 bytes of K per step; lane l holds row
+// l % 16, K bytes 16 (l / 16) .. +15, and D[i][j] sits in lane j + 16 (i / 4),
+// register i % 4.
+template <int MF>
+struct Mfma;
+template <>
+struct Mfma<32> {
+  using Acc = v16i;
+  static constexpr int kStepBytes = 32, kGroups = 4;
+  static __device__ __forceinline__ Acc run(v4i a, v4i b, Acc c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct Mfma<16> {
+  using Acc = v4i;
+  static constexpr int kStepBytes = 64, kGroups = 1;
+  static __device__ __forceinline__ Acc run(v4i a, v4i b, Acc c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int MF_>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int BK = 128;                    // bytes of K per stage
-  static constexpr int kSlots = BK / 16;            // 16-byte chunks per row
-  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int MF = MF_;
+  using Op = Mfma<MF>;
+  using Acc = typename Op::Acc;
+  static constexpr int kSlots = BK / 16;            // 16-byte chunks per LDS row
+  static constexpr int kSteps = BK / Op::kStepBytes;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int TM = BM / WM, TN = BN / WN;  // per-wave tile
-  static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 MFMA blocks per wave
-  static constexpr int kWChunks = BN * kSlots;
-  static constexpr int kXChunks = BM * kSlots;
-  static constexpr int kWPer = (kWChunks + kThreads - 1) / kThreads;
-  static constexpr int kXPer = (kXChunks + kThreads - 1) / kThreads;
+  static constexpr int FM = TM / MF, FN = TN / MF;  // MFMA blocks per wave
+  static constexpr int kRowsPerLoad = 1024 / BK;    // rows one wave instruction fills
+  static constexpr int kLoads = (BM + BN) / kRowsPerLoad;  // per stage, whole workgroup
+  static constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
   static constexpr int kStage = (BM + BN) * BK;     // LDS bytes per stage
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be whole MFMA blocks");
-  static_assert(2 * kStage <= 160 * 1024, "LDS budget");
+  static_assert(BK == 64 || BK == 128, "BK");
+  static_assert(kSteps >= 2 && kSteps % 2 == 0, "fragment sets alternate within a stage");
+  static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be whole MFMA blocks");
+  static_assert(BN % 16 == 0 && BM % 16 == 0 && BM % kRowsPerLoad == 0, "load blocks");
+  static_assert((BN / kRowsPerLoad) % kWaves == 0 || kLoads <= kWaves,
+                "a load slot of a wave is all weight rows or all activation rows");
+  // deeper pipelines count each wave's own loads in vmcnt waits, so every
+  // wave must issue the same number per stage; 2-stage pipelines wait for 0
+  static_assert(STAGES == 2 || kLoads % kWaves == 0, "uneven loads need a 2-stage pipeline");
+  static_assert(STAGES >= 2 && STAGES * kStage <= 160 * 1024, "LDS budget");
 };
 
 // Map a linear tile index to (tile_m, tile_n): XCD-contiguous ranges, then
@@ -77,87 +127,156 @@ __device__ __forceinline__ void tile_coords(int t, int T, int MT, int NT, int& t
   tn = r / gsz;
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8).  Issued through the builtin so that the compiler's own
+// wait insertion knows about them and does not add conservative waits.
+template <int VM, int LGKM>
+constexpr int waitcnt_imm() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "counter range");
+  return (VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (LGKM << 8);
+}
+
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(waitcnt_imm<0, 15>()); }
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<N, 15>());
+}
+
+// Wait until at most `ahead` stages of this wave's loads are outstanding.
 template <class C>
-struct Stage {
-  uint4 w[C::kWPer];
-  uint4 x[C::kXPer];
+__device__ __forceinline__ void wait_stages(int ahead) {
+  constexpr int L = C::kLoadsPerWave;
+  if constexpr (C::STAGES >= 3) {
+    if (ahead >= 1) {
+      if constexpr (C::STAGES >= 4) {
+        if (ahead >= 2) {
+          if constexpr (C::STAGES >= 5) {
+            if (ahead >= 3) { wait_vm<3 * L>(); return; }
+          }
+          wait_vm<2 * L>();
+          return;
+        }
+      }
+      wait_vm<L>();
+      return;
+    }
+  }
+  wait_vm0();
+}
+
+// All waves of the workgroup: this wave's LDS reads done, then everyone
+// arrives.  (No vmcnt wait: later stages stay in flight.)
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<63, 0>());
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A uniform 64-bit value forced into scalar registers.  It also stops the
+// compiler from folding per-lane offsets into hoisted 64-bit vector addresses.
+__device__ __forceinline__ const int8_t* sgpr_ptr(const int8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const int8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Stage loads.  Block j of a stage covers rows [j R, (j+1) R) of the
+// concatenated [BN weight rows | BM activation rows] tile, R = 1024 / BK;
+// lane i fills row j R + i / SLOTS at physical slot i % SLOTS, i.e. it loads
+// logical chunk swz(row, slot) (the swizzle is an involution).  FAST (interior
+// tile, K a multiple of BK): a scalar base per block plus one per-lane
+// offset.  Otherwise rows and chunks are clamped into the operands per lane
+// (clamped data only feeds outputs that are never stored, or meets a zeroed
+// activation fragment).
+template <class C, bool FAST>
+struct Loader {
+  static constexpr int R = C::kRowsPerLoad;
+  static constexpr int kWBlocksPerWave = C::BN / R / C::kWaves;  // leading weight slots
+  const int8_t* qw;
+  const int8_t* qx;
+  int64_t n0, m0, M, N, K;
+  uint32_t lane_off;
+
+  __device__ __forceinline__ Loader(const GemmArgs& a, int64_t n0_, int64_t m0_, int wave, int lane)
+      : qw(a.qw), qx(a.qx), n0(n0_), m0(m0_), M(a.M), N(a.N), K(a.K) {
+    const int lr = lane / C::kSlots, p = lane % C::kSlots;
+    // row & 15 of this wave's blocks: (j R) & 15 + lr, j = wave + jj kWaves
+    const int rbase = (R == 8) ? ((wave & 1) * 8) : 0;
+    lane_off = static_cast<uint32_t>(lr * K + swz<C::kSlots>(rbase + lr, p) * 16);
+  }
+
+  int koff = 0, kst = 1;  // K-stage rotation (see run_tile)
+
+  __device__ __forceinline__ void issue(int s, int8_t* dst, int wave, int lane) const {
+    int ks = s + koff;
+    if (ks >= kst) ks -= kst;
+    const int64_t k0 = static_cast<int64_t>(ks) * C::BK;
+#pragma unroll
+    for (int jj = 0; jj < C::kLoadsPerWave; ++jj) {
+      const int j = wave + jj * C::kWaves;
+      if (C::kLoads % C::kWaves != 0 && j >= C::kLoads) break;
+      const bool is_w = jj < kWBlocksPerWave;  // compile-time after unrolling
+      const int row0 = is_w ? j * R : j * R - C::BN;
+      const int8_t* op = is_w ? qw : qx;
+      const int64_t g0 = (is_w ? n0 : m0) + row0;
+      lds_void* d = (lds_void*)(dst + j * 1024);
+      if constexpr (FAST) {
+        const int8_t* g = sgpr_ptr(op + g0 * K + k0) + lane_off;
+        __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
+      } else {
+        const int lr = lane / C::kSlots, p = lane % C::kSlots;
+        int64_t row = g0 + lr;
+        const int64_t lim = is_w ? N : M;
+        if (row > lim - 1) row = lim - 1;
+        int64_t k = k0 + swz<C::kSlots>(row0 + lr, p) * 16;
+        if (k > K - 16) k = K - 16;
+        const int8_t* g = op + row * K + k;
+        __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
+      }
+    }
+  }
 };
 
-// Global -> registers for one K stage (zero-filled outside the matrices).
 template <class C>
-__device__ __forceinline__ void load_stage(Stage<C>& st, const int8_t* __restrict__ qw,
-                                           const int8_t* __restrict__ qx, int64_t n0, int64_t m0,
-                                           int64_t k0, int64_t M, int64_t N, int64_t K) {
-  const int t = threadIdx.x;
+struct Frags {
+  v4i w[C::FN];
+  v4i x[C::FM];
+};
+
+// Fragments of one k-step: lane reads row (MF f + lane % MF) of its wave tile
+// at the lane's chunk; lw / lx: lane + wave part of the address.
+template <class C>
+__device__ __forceinline__ void read_frags(Frags<C>& fr, const int8_t* stage, uint32_t lw,
+                                           uint32_t lx) {
+  const int8_t* sw = stage + lw;
+  const int8_t* sx = stage + lx;
 #pragma unroll
-  for (int j = 0; j < C::kWPer; ++j) {
-    const int i = t + j * C::kThreads;
-    const int r = i / C::kSlots, c = i % C::kSlots;
-    const int64_t n = n0 + r, k = k0 + c * 16;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (i < C::kWChunks && n < N && k < K) v = *reinterpret_cast<const uint4*>(qw + n * K + k);
-    st.w[j] = v;
-  }
+  for (int f = 0; f < C::FN; ++f) fr.w[f] = *reinterpret_cast<const v4i*>(sw + f * C::MF * C::BK);
 #pragma unroll
-  for (int j = 0; j < C::kXPer; ++j) {
-    const int i = t + j * C::kThreads;
-    const int r = i / C::kSlots, c = i % C::kSlots;
-    const int64_t m = m0 + r, k = k0 + c * 16;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (i < C::kXChunks && m < M && k < K) v = *reinterpret_cast<const uint4*>(qx + m * K + k);
-    st.x[j] = v;
-  }
+  for (int f = 0; f < C::FM; ++f) fr.x[f] = *reinterpret_cast<const v4i*>(sx + f * C::MF * C::BK);
 }
 
-// Registers -> LDS (swizzled).  sW: BN rows, sX: BM rows, 128 B each.
-template <class C>
-__device__ __forceinline__ void store_stage(const Stage<C>& st, int8_t* sW, int8_t* sX) {
-  const int t = threadIdx.x;
+// MFMAs of one k-step, weight-fragment rows [I0, I1).
+template <class C, int I0, int I1>
+__device__ __forceinline__ void mfma_rows(const Frags<C>& fr, typename C::Acc (&acc)[C::FN][C::FM]) {
 #pragma unroll
-  for (int j = 0; j < C::kWPer; ++j) {
-    const int i = t + j * C::kThreads;
-    if (i < C::kWChunks) {
-      const int r = i / C::kSlots, c = i % C::kSlots;
-      *reinterpret_cast<uint4*>(sW + r * C::BK + swz(r, c) * 16) = st.w[j];
-    }
-  }
+  for (int i = I0; i < I1; ++i)
 #pragma unroll
-  for (int j = 0; j < C::kXPer; ++j) {
-    const int i = t + j * C::kThreads;
-    if (i < C::kXChunks) {
-      const int r = i / C::kSlots, c = i % C::kSlots;
-      *reinterpret_cast<uint4*>(sX + r * C::BK + swz(r, c) * 16) = st.x[j];
-    }
-  }
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = C::Op::run(fr.w[i], fr.x[j], acc[i][j]);
 }
 
-// MFMAs over one LDS stage.
 template <class C>
-__device__ __forceinline__ void compute_stage(const int8_t* sW, const int8_t* sX, int wn, int wm,
-                                              v4i (&acc)[C::FN][C::FM]) {
-  const int lane = threadIdx.x & 63;
-  const int lr = lane & 15, lq = lane >> 4;
-#pragma unroll
-  for (int kk = 0; kk < C::BK / 64; ++kk) {
-    const int c = kk * 4 + lq;
-    v4i a[C::FN], b[C::FM];
-#pragma unroll
-    for (int f = 0; f < C::FN; ++f) {
-      const int r = wn * C::TN + f * 16 + lr;
-      a[f] = *reinterpret_cast<const v4i*>(sW + r * C::BK + swz(r, c) * 16);
-    }
-#pragma unroll
-    for (int f = 0; f < C::FM; ++f) {
-      const int r = wm * C::TM + f * 16 + lr;
-      b[f] = *reinterpret_cast<const v4i*>(sX + r * C::BK + swz(r, c) * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
+__device__ __forceinline__ void mfma_step(const Frags<C>& fr, typename C::Acc (&acc)[C::FN][C::FM]) {
+  mfma_rows<C, 0, C::FN>(fr, acc);
 }
+
+// Keep the compiler's scheduler from moving instructions across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// All of this wave's LDS reads have landed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(waitcnt_imm<63, 0>()); }
 
 __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
@@ -170,93 +289,333 @@ __device__ __forceinline__ float dequant(int32_t acc, float sx, float sw, float 
   return has_bias ? v + b : v;
 }
 
+// Lane owns, in each MFMA block, output row m = lane % MF and four runs of
+// four consecutive columns (one run for MF = 16).
+template <class C, bool OUT_I32, bool GUARD>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t n0, int wn, int wm,
+                                         int lane, const typename C::Acc (&acc)[C::FN][C::FM]) {
+  constexpr int MF = C::MF;
+  constexpr int G = C::Op::kGroups;
+  const int64_t M = a.M, N = a.N;
+  const int lr = lane % MF, lq = lane / MF;
+  const bool hb = a.bias != nullptr;
+#pragma unroll
+  for (int fi = 0; fi < C::FN; ++fi) {
+    const int64_t nb = n0 + wn * C::TN + fi * MF + lq * 4;
+    float sw[G][4], bv[G][4];
+    if constexpr (!OUT_I32) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t n = nb + g * 8 + e;
+          const bool in = !GUARD || n < N;
+          sw[g][e] = in ? a.sw[n] : 0.0f;
+          bv[g][e] = (hb && in) ? __uint_as_float(static_cast<uint32_t>(a.bias[n]) << 16) : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int fj = 0; fj < C::FM; ++fj) {
+      // one block at a time: keeps the scheduler from pulling every
+      // accumulator out of the AGPRs at once
+      __builtin_amdgcn_sched_barrier(0);
+      const int64_t m = m0 + wm * C::TM + fj * MF + lr;
+      if (GUARD && m >= M) continue;
+      const typename C::Acc d = acc[fi][fj];
+      const float sx = OUT_I32 ? 0.0f : a.sx[m];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t n = nb + g * 8;
+        if (GUARD && n >= N) continue;
+        const bool vec = !GUARD || ((N % 4) == 0 && n + 3 < N);
+        if constexpr (OUT_I32) {
+          int32_t* out = static_cast<int32_t*>(a.out) + m * N + n;
+          if (vec) {
+            *reinterpret_cast<v4i*>(out) = v4i{d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]};
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) out[e] = d[4 * g + e];
+          }
+        } else {
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = bf16_bits(dequant(d[4 * g + e], sx, sw[g][e], bv[g][e], hb));
+          uint16_t* out = static_cast<uint16_t*>(a.out) + m * N + n;
+          if (vec) {
+            uint2 pk;
+            pk.x = h[0] | (h[1] << 16);
+            pk.y = h[2] | (h[3] << 16);
+            *reinterpret_cast<uint2*>(out) = pk;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) out[e] = static_cast<uint16_t>(h[e]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Interior-tile bf16 epilogue through LDS: each wave dequantizes its
+// accumulators in the MFMA layout and writes 8-byte runs (4 outputs) into a
+// row-major staging tile; then every wave writes whole output rows, 8 bytes
+// per lane, so each store instruction covers BN / 4 lanes' worth of
+// contiguous row bytes (a full 512-byte row for BN = 256).  Staging slots of
+// 8 bytes are XOR-swizzled with the row: the MFMA-layout writes (32 rows at
+// one slot) and the row reads (one row, consecutive slots) are both free of
+// bank conflicts.
+// Interior-tile bf16 epilogue, stored straight from the MFMA layout.  All
+// scales and biases the lane needs are fetched up front with vector loads
+// (four consecutive columns per 16-byte s_w load and 8-byte bias load; both
+// vectors are aligned on this path), then each accumulator block is
+// dequantized and written as 8-byte runs.
+template <class C>
+__device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int64_t n0, int wn,
+                                              int wm, int lane,
+                                              const typename C::Acc (&acc)[C::FN][C::FM]) {
+  constexpr int MF = C::MF;
+  constexpr int G = C::Op::kGroups;
+  const int lr = lane % MF, lq = lane / MF;
+  const bool hb = a.bias != nullptr;
+  float sx[C::FM];
+#pragma unroll
+  for (int fj = 0; fj < C::FM; ++fj) sx[fj] = a.sx[m0 + wm * C::TM + fj * MF + lr];
+  float4 sw[C::FN][G];
+  uint2 bb[C::FN][G];
+#pragma unroll
+  for (int fi = 0; fi < C::FN; ++fi)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
+      sw[fi][g] = *reinterpret_cast<const float4*>(a.sw + n);
+      bb[fi][g] = hb ? *reinterpret_cast<const uint2*>(a.bias + n) : make_uint2(0u, 0u);
+    }
+  uint16_t* y = static_cast<uint16_t*>(a.out);
+#pragma unroll
+  for (int fi = 0; fi < C::FN; ++fi) {
+#pragma unroll
+    for (int fj = 0; fj < C::FM; ++fj) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int64_t m = m0 + wm * C::TM + fj * MF + lr;
+      const typename C::Acc d = acc[fi][fj];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
+        const float swv[4] = {sw[fi][g].x, sw[fi][g].y, sw[fi][g].z, sw[fi][g].w};
+        const float bv[4] = {__uint_as_float(bb[fi][g].x << 16), __uint_as_float(bb[fi][g].x & 0xFFFF0000u),
+                             __uint_as_float(bb[fi][g].y << 16), __uint_as_float(bb[fi][g].y & 0xFFFF0000u)};
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = bf16_bits(dequant(d[4 * g + e], sx[fj], swv[e], bv[e], hb));
+        uint2 pk;
+        pk.x = h[0] | (h[1] << 16);
+        pk.y = h[2] | (h[3] << 16);
+        *reinterpret_cast<uint2*>(y + m * a.N + n) = pk;
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ int stage_slot(int row, int slot) {
+  constexpr int SLOTS = C::BN / 4;  // 8-byte slots per staged row
+  constexpr int MASK = SLOTS >= 32 ? 31 : SLOTS - 1;
+  return slot ^ (row & MASK);
+}
+
+template <class C>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& a, int8_t* smem, int64_t m0, int64_t n0,
+                                             int wn, int wm, int wave, int lane,
+                                             const typename C::Acc (&acc)[C::FN][C::FM]) {
+  constexpr int MF = C::MF;
+  constexpr int G = C::Op::kGroups;
+  constexpr int SLOTS = C::BN / 4;
+  static_assert(C::BM * C::BN * 2 <= C::STAGES * C::kStage, "staging tile fits the LDS stages");
+  const int lr = lane % MF, lq = lane / MF;
+  const bool hb = a.bias != nullptr;
+  block_barrier();  // all waves are done reading the operand stages
+#pragma unroll
+  for (int fi = 0; fi < C::FN; ++fi) {
+    const int nl = wn * C::TN + fi * MF + lq * 4;  // local column of run g = 0
+    float sw[G][4], bv[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t n = n0 + nl + g * 8 + e;
+        sw[g][e] = a.sw[n];
+        bv[g][e] = hb ? __uint_as_float(static_cast<uint32_t>(a.bias[n]) << 16) : 0.0f;
+      }
+#pragma unroll
+    for (int fj = 0; fj < C::FM; ++fj) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int ml = wm * C::TM + fj * MF + lr;
+      const float sx = a.sx[m0 + ml];
+      const typename C::Acc d = acc[fi][fj];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        uint32_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = bf16_bits(dequant(d[4 * g + e], sx, sw[g][e], bv[g][e], hb));
+        uint2 pk;
+        pk.x = h[0] | (h[1] << 16);
+        pk.y = h[2] | (h[3] << 16);
+        const int slot = (nl + g * 8) / 4;
+        *reinterpret_cast<uint2*>(smem + ml * (C::BN * 2) + stage_slot<C>(ml, slot) * 8) = pk;
+      }
+    }
+  }
+  block_barrier();
+  // rows out: wave instruction i covers rows (wave + i * kWaves) * RPW .. + RPW
+  constexpr int RPW = 64 / SLOTS > 0 ? 64 / SLOTS : 1;  // rows per wave instruction
+  static_assert(SLOTS <= 64 && 64 % SLOTS == 0, "staged row is a whole number of lanes");
+  const int rsub = lane / SLOTS, slot = lane % SLOTS;
+  uint16_t* y = static_cast<uint16_t*>(a.out);
+#pragma unroll 4
+  for (int r0 = wave * RPW; r0 < C::BM; r0 += C::kWaves * RPW) {
+    const int row = r0 + rsub;
+    const uint2 v = *reinterpret_cast<const uint2*>(smem + row * (C::BN * 2) + stage_slot<C>(row, slot) * 8);
+    *reinterpret_cast<uint2*>(y + (m0 + row) * a.N + n0 + slot * 4) = v;
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void zero_tail(Frags<C>& fr, int64_t kstep0, int64_t K, int lane) {
+  if (kstep0 + (lane / C::MF) * 16 >= K) {
+#pragma unroll
+    for (int f = 0; f < C::FM; ++f) fr.x[f] = v4i{0, 0, 0, 0};
+  }
+}
+
+// One output tile: prologue loads, the K loop, the epilogue.
+template <class C, bool FAST, bool OUT_I32>
+__device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_t m0, int64_t n0,
+                                         int tile_m, int tile_n, int wave, int lane) {
+  constexpr int S = C::STAGES;
+  constexpr int NS = C::kSteps;
+  constexpr int SB = C::Op::kStepBytes;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  const int KST = static_cast<int>((a.K + C::BK - 1) / C::BK);  // stages
+
+  Loader<C, FAST> ld(a, n0, m0, wave, lane);
+  // Tiles that share an operand panel run their K loops from different
+  // starting stages (integer accumulation is order-independent, so the result
+  // is the same bit for bit): the first tile to reach a panel stage fetches it,
+  // the others find it in L2 a few stages later instead of all waiting on the
+  // same in-flight misses.  Only whole-stage (FAST) tiles rotate.
+  ld.kst = KST;
+  if constexpr (FAST) ld.koff = KST > 0 ? static_cast<int>(((tile_n + 2 * tile_m) % 8) * 2 % KST) : 0;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (s < KST) ld.issue(s, smem + s * C::kStage, wave, lane);
+
+  // fragment addressing: row (MF f + lane % MF), chunk (step SB/16 + lane / MF)
+  uint32_t lw[NS], lx[NS];
+  {
+    const int fr = lane % C::MF, fq = lane / C::MF;
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) {
+      const uint32_t l = static_cast<uint32_t>(fr * C::BK + swz<C::kSlots>(fr, ks * (SB / 16) + fq) * 16);
+      lw[ks] = l + static_cast<uint32_t>(wn * C::TN * C::BK);
+      lx[ks] = l + static_cast<uint32_t>(C::BN * C::BK + wm * C::TM * C::BK);
+    }
+  }
+
+  typename C::Acc acc[C::FN][C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = typename C::Acc{};
+
+  if (KST > 0) {
+    wait_stages<C>(min(S - 1, KST - 1));  // stage 0 landed
+    block_barrier();
+    Frags<C> f[2];
+    read_frags<C>(f[0], smem, lw[0], lx[0]);
+    // Full stages; the last (possibly partial) stage is peeled below.
+    // Software pipeline per k-step: make sure this step's fragments have
+    // landed (they were read a whole step earlier), read the next step's
+    // fragments, then issue this step's MFMAs -- the reads get a full MFMA
+    // batch of lead time.  The last step of a stage first opens the next
+    // stage (its loads landed everywhere, then a barrier), and issues the
+    // loads that refill the freed buffer after a quarter of its MFMAs.
+    constexpr int FQ = (C::FN >= 4) ? C::FN / 4 : 1;  // MFMA rows before the load issue
+    for (int st = 0; st < KST - 1; ++st) {
+      const int8_t* cur = smem + (st % S) * C::kStage;
+#pragma unroll
+      for (int ks = 0; ks < NS; ++ks) {
+        Frags<C>& fc = f[ks & 1];
+        Frags<C>& fn = f[(ks + 1) & 1];
+        sched_fence();
+        wait_lds();
+        if (ks + 1 < NS) {
+          read_frags<C>(fn, cur, lw[ks + 1], lx[ks + 1]);
+          sched_fence();
+          mfma_rows<C, 0, C::FN>(fc, acc);
+        } else {
+          wait_stages<C>(min(S - 2, KST - 2 - st));  // stage st+1 landed (this wave)
+          block_barrier();                           // ... everywhere; stage st is free
+          read_frags<C>(fn, smem + ((st + 1) % S) * C::kStage, lw[0], lx[0]);
+          sched_fence();
+          mfma_rows<C, 0, FQ>(fc, acc);
+          sched_fence();
+          if (st + S < KST) ld.issue(st + S, smem + (st % S) * C::kStage, wave, lane);
+          sched_fence();
+          mfma_rows<C, FQ, C::FN>(fc, acc);
+        }
+      }
+    }
+    {
+      const int st = KST - 1;
+      const int8_t* cur = smem + (st % S) * C::kStage;
+      const int64_t k0 = static_cast<int64_t>(st) * C::BK;
+#pragma unroll
+      for (int ks = 0; ks < NS; ++ks) {
+        const int64_t ksk = k0 + ks * SB;
+        if (!FAST && ksk >= a.K) break;
+        sched_fence();
+        wait_lds();
+        if (ks + 1 < NS && (FAST || ksk + SB < a.K))
+          read_frags<C>(f[(ks + 1) & 1], cur, lw[ks + 1], lx[ks + 1]);
+        if (!FAST && ksk + SB > a.K) zero_tail<C>(f[ks & 1], ksk, a.K, lane);
+        sched_fence();
+        mfma_step<C>(f[ks & 1], acc);
+      }
+    }
+  }
+#ifndef W8A8_LDS_EPILOGUE
+  if constexpr (FAST && !OUT_I32)
+    epilogue_fast<C>(a, m0, n0, wn, wm, lane, acc);
+#else
+  if constexpr (FAST && !OUT_I32)
+    epilogue_lds<C>(a, smem, m0, n0, wn, wm, wave, lane, acc);
+#endif
+  else
+    epilogue<C, OUT_I32, !FAST>(a, m0, n0, wn, wm, lane, acc);
+}
+
 template <class C, bool OUT_I32>
 __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, int MT, int NT) {
-  __shared__ __attribute__((aligned(16))) int8_t smem[2 * C::kStage];
-  const int wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[C::STAGES * C::kStage];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int wn = wave % C::WN, wm = wave / C::WN;
-  const int64_t M = a.M, N = a.N, K = a.K;
-  const int KT = static_cast<int>((K + C::BK - 1) / C::BK);
-
+  // normally one tile per workgroup; grids are capped for huge problems
   for (int t = blockIdx.x; t < T; t += gridDim.x) {
     int tm, tn;
     tile_coords(t, T, MT, NT, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * C::BM;
     const int64_t n0 = static_cast<int64_t>(tn) * C::BN;
-
-    v4i acc[C::FN][C::FM];
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-    if (KT > 0) {
-      Stage<C> st;
-      load_stage<C>(st, a.qw, a.qx, n0, m0, 0, M, N, K);
-      store_stage<C>(st, smem, smem + C::BN * C::BK);
-      __syncthreads();
-      for (int kt = 0; kt < KT; ++kt) {
-        int8_t* cur = smem + (kt & 1) * C::kStage;
-        int8_t* nxt = smem + ((kt + 1) & 1) * C::kStage;
-        const bool more = (kt + 1 < KT);
-        if (more) load_stage<C>(st, a.qw, a.qx, n0, m0, static_cast<int64_t>(kt + 1) * C::BK, M, N, K);
-        compute_stage<C>(cur, cur + C::BN * C::BK, wn, wm, acc);
-        if (more) store_stage<C>(st, nxt, nxt + C::BN * C::BK);
-        __syncthreads();
-      }
-    }
-
-    // Epilogue: lane owns D[n = 4*lq + i][m = lr] of each 16x16 block.
-    const int lr = lane & 15, lq = lane >> 4;
-    const bool vec_ok = (N % 4) == 0;
-#pragma unroll
-    for (int fi = 0; fi < C::FN; ++fi) {
-      const int64_t n = n0 + wn * C::TN + fi * 16 + lq * 4;
-      float sw[4], bv[4];
-      if constexpr (!OUT_I32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sw[i] = (n + i < N) ? a.sw[n + i] : 0.0f;
-          bv[i] = (a.bias != nullptr && n + i < N) ? __uint_as_float(static_cast<uint32_t>(a.bias[n + i]) << 16) : 0.0f;
-        }
-      }
-#pragma unroll
-      for (int fj = 0; fj < C::FM; ++fj) {
-        const int64_t m = m0 + wm * C::TM + fj * 16 + lr;
-        if (m >= M || n >= N) continue;
-        const v4i d = acc[fi][fj];
-        if constexpr (OUT_I32) {
-          int32_t* out = static_cast<int32_t*>(a.out) + m * N + n;
-          if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<v4i*>(out) = d;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (n + i < N) out[i] = d[i];
-          }
-        } else {
-          const float sx = a.sx[m];
-          const bool hb = a.bias != nullptr;
-          uint32_t h[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = bf16_bits(dequant(d[i], sx, sw[i], bv[i], hb));
-          uint16_t* out = static_cast<uint16_t*>(a.out) + m * N + n;
-          if (vec_ok && n + 3 < N) {
-            uint2 p;
-            p.x = h[0] | (h[1] << 16);
-            p.y = h[2] | (h[3] << 16);
-            *reinterpret_cast<uint2*>(out) = p;
-          } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (n + i < N) out[i] = static_cast<uint16_t>(h[i]);
-          }
-        }
-      }
-    }
-    // the next tile's prologue overwrites stage 0 of the LDS
-    __syncthreads();
+    // interior tile, whole stages in K, and vector-aligned scales / bias
+    const bool fast = (m0 + C::BM <= a.M) && (n0 + C::BN <= a.N) && (a.N % 4 == 0) &&
+                      (a.K % C::BK == 0) && (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
+                      (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0);
+    if (t != static_cast<int>(blockIdx.x)) block_barrier();  // LDS reuse across tiles
+    if (fast)
+      run_tile<C, true, OUT_I32>(a, smem, m0, n0, tm, tn, wave, lane);
+    else
+      run_tile<C, false, OUT_I32>(a, smem, m0, n0, tm, tn, wave, lane);
   }
 }
 
@@ -264,39 +623,43 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
 struct ConfigInfo {
   const char* name;
   int BM, BN, threads;
-  int wg_per_cu;   // workgroups that fit on one CU (LDS / register bound)
-  float rel_speed; // relative per-CU throughput when the chip is full
+  int wg_per_cu;   // workgroups resident per CU (LDS / register bound)
+  float rel_speed; // relative per-CU throughput with the chip full
 };
 
-using T256x256 = Tile<256, 256, 2, 4>;  // 8 waves, wave tile 128(m) x 64(n)
-using T256x128 = Tile<256, 128, 4, 2>;  // 8 waves, wave tile 64 x 64
-using T128x256 = Tile<128, 256, 2, 4>;  // 8 waves, wave tile 64 x 64
-using T128x128 = Tile<128, 128, 2, 2>;  // 4 waves, wave tile 64 x 64
-using T64x64 = Tile<64, 64, 2, 2>;      // 4 waves, wave tile 32 x 32
-using T16x64 = Tile<16, 64, 1, 4>;      // 4 waves, wave tile 16 x 16 (skinny M)
+//             BM   BN  WM WN  BK  STAGES MFMA
+using C0 = Tile<256, 256, 2, 2, 64, 4, 32>;   // 4 waves, wave tile 128 x 128
+using C1 = Tile<256, 256, 2, 2, 128, 2, 32>;  // same, 2 deep stages
+using C2 = Tile<256, 128, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 64(n)
+using C3 = Tile<128, 256, 2, 2, 64, 4, 32>;   // wave tile 64(m) x 128(n)
+using C4 = Tile<128, 128, 2, 2, 64, 4, 32>;   // wave tile 64 x 64
+using C5 = Tile<64, 64, 2, 2, 128, 2, 32>;    // wave tile 32 x 32
+using C6 = Tile<16, 64, 1, 4, 128, 2, 16>;    // wave tile 16 x 16 (skinny M)
 
 const ConfigInfo kConfigs[] = {
-    {"bm256_bn256_bk128_w2x4", 256, 256, 512, 1, 1.00f},
-    {"bm256_bn128_bk128_w4x2", 256, 128, 512, 1, 0.90f},
-    {"bm128_bn256_bk128_w2x4", 128, 256, 512, 1, 0.90f},
-    {"bm128_bn128_bk128_w2x2", 128, 128, 256, 2, 0.80f},
-    {"bm64_bn64_bk128_w2x2", 64, 64, 256, 4, 0.45f},
-    {"bm16_bn64_bk128_w1x4", 16, 64, 256, 4, 0.20f},
+    {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 1.00f},
+    {"bm256_bn256_bk128_s2_mf32", 256, 256, 256, 1, 0.98f},
+    {"bm256_bn128_bk64_s4_mf32", 256, 128, 256, 1, 0.85f},
+    {"bm128_bn256_bk64_s4_mf32", 128, 256, 256, 1, 0.85f},
+    {"bm128_bn128_bk64_s4_mf32", 128, 128, 256, 2, 0.70f},
+    {"bm64_bn64_bk128_s2_mf32", 64, 64, 256, 4, 0.40f},
+    {"bm16_bn64_bk128_s2_mf16", 16, 64, 256, 4, 0.15f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-constexpr int kNumCU = 256;
-constexpr int kMaxGrid = 1 << 20;
+constexpr int kSkinny = kNumConfigs - 1;
+constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
 template <class C, bool I32>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t MT = (a.M + C::BM - 1) / C::BM;
   const int64_t NT = (a.N + C::BN - 1) / C::BN;
   const int64_t T = MT * NT;
-  if (T > INT32_MAX || MT > INT32_MAX || NT > INT32_MAX) return hipErrorInvalidValue;
-  const int grid = static_cast<int>(T < kMaxGrid ? T : kMaxGrid);
-  gemm_kernel<C, I32><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(a, static_cast<int>(T),
-                                                                   static_cast<int>(MT),
-                                                                   static_cast<int>(NT));
+  if (T > INT32_MAX) return hipErrorInvalidValue;
+  // grid x threads must stay below 2^32 work-items; a multiple of the 8 XCDs
+  const int64_t cap = ((0xFFFFFFFFll / C::kThreads) / 8) * 8;
+  const int grid = static_cast<int>(T < cap ? T : cap);
+  gemm_kernel<C, I32><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
+      a, static_cast<int>(T), static_cast<int>(MT), static_cast<int>(NT));
   return hipGetLastError();
 }
 
@@ -315,10 +678,11 @@ const char* gemm_config_name(int cfg) {
 
 // Per-shape choice: the configuration with the least estimated time, where a
 // configuration's time is (number of full-chip waves of tiles) x (tile area)
-// / (its relative per-CU throughput).  Skinny M (<= 16) takes the narrow tile.
+// x (workgroups sharing a CU) / (relative per-CU throughput).  Skinny M
+// (<= 16) takes the narrow tile.
 int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   (void)K;
-  if (M <= 16) return 5;
+  if (M <= 16) return kSkinny;
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < kNumConfigs - 1; ++c) {
@@ -337,13 +701,15 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
 }
 
 hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t stream) {
+  if (cfg < 0 || cfg >= kNumConfigs) return hipErrorInvalidValue;
   switch (cfg) {
-    case 0: return launch_cfg_out<T256x256>(a, out_int32, stream);
-    case 1: return launch_cfg_out<T256x128>(a, out_int32, stream);
-    case 2: return launch_cfg_out<T128x256>(a, out_int32, stream);
-    case 3: return launch_cfg_out<T128x128>(a, out_int32, stream);
-    case 4: return launch_cfg_out<T64x64>(a, out_int32, stream);
-    case 5: return launch_cfg_out<T16x64>(a, out_int32, stream);
+    case 0: return launch_cfg_out<C0>(a, out_int32, stream);
+    case 1: return launch_cfg_out<C1>(a, out_int32, stream);
+    case 2: return launch_cfg_out<C2>(a, out_int32, stream);
+    case 3: return launch_cfg_out<C3>(a, out_int32, stream);
+    case 4: return launch_cfg_out<C4>(a, out_int32, stream);
+    case 5: return launch_cfg_out<C5>(a, out_int32, stream);
+    case 6: return launch_cfg_out<C6>(a, out_int32, stream);
     default: return hipErrorInvalidValue;
   }
 }
