@@ -51,6 +51,11 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time every GEMM configuration on every workload shape instead")
     ap.add_argument("--sweep-iters", type=int, default=20)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device-to-device copy of known size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of a bench run and of a "
+                         "--copy-calibration run): write the up-proj GEMM's HBM bytes per launch")
     return ap.parse_args()
 
 
@@ -70,6 +75,73 @@ def traffic_entry():
     if t.get("gemm_src_sha256_16") != gemm_src_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+COPY_BYTES = 512 << 20  # bytes read and bytes written by one calibration copy
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of COPY_BYTES, run a few times: the
+    counters FETCH_SIZE / WRITE_SIZE read for it calibrate the GEMM's."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 5}))
+
+
+def _counter_rows(folder, counter):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append(r)
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {folder}")
+    return rows
+
+
+def write_traffic(gf, gw, cf, cw):
+    """Per-launch HBM bytes of the up-proj GEMM (the dispatch of the gemm kernel
+    with the up-proj grid) from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by bytes-moved / counter-reading of the calibration copy."""
+    def copy_factor(folder, counter):
+        vals = [float(r["Counter_Value"]) * 1024 for r in _counter_rows(folder, counter)
+                if "copy" in r["Kernel_Name"].lower() or "elementwise" in r["Kernel_Name"].lower()]
+        if not vals:
+            raise SystemExit(f"no copy kernel rows for {counter} in {folder}")
+        return max(vals) / COPY_BYTES  # counter bytes per real byte
+
+    import re
+
+    import w8a8_int8_quantized_quantize_amd as w8
+    name = w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(4096, 12288, 3072))
+    bm, bn = (int(v) for v in re.match(r"bm(\d+)_bn(\d+)_", name).groups())
+    grid_up = ((4096 + bm - 1) // bm) * ((12288 + bn - 1) // bn) * 256  # work-items
+
+    def gemm_bytes(folder, counter):
+        vals = [float(r["Counter_Value"]) * 1024 for r in _counter_rows(folder, counter)
+                if "gemm_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) == grid_up]
+        if not vals:
+            raise SystemExit(f"no up-proj gemm rows for {counter} in {folder}")
+        return sum(vals) / len(vals), len(vals)
+
+    ff, fw = copy_factor(cf, "FETCH_SIZE"), copy_factor(cw, "WRITE_SIZE")
+    (fb, nf), (wb, nw) = gemm_bytes(gf, "FETCH_SIZE"), gemm_bytes(gw, "WRITE_SIZE")
+    out = {"kernel": f"gemm_kernel ({name}), up-proj M=4096 K=3072 N=12288",
+           "gemm_src_sha256_16": gemm_src_hash(),
+           "fetch_bytes_per_launch": fb / ff, "write_bytes_per_launch": wb / fw,
+           "bytes_per_launch": fb / ff + wb / fw,
+           "raw_fetch_size_kib": fb / 1024, "raw_write_size_kib": wb / 1024,
+           "copy_factor_fetch": ff, "copy_factor_write": fw, "launches": [nf, nw],
+           "algorithmic_bytes_per_launch": 4096 * 3072 + 12288 * 3072 + 6 * 12288 + 4 * 4096 + 2 * 4096 * 12288}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def make_inputs(torch, w8, synthetic, rotate):
@@ -125,7 +197,9 @@ def cpu_baseline(up, down, seconds):
         oracle.linear(h, wdq, wds, bd)
         return time.perf_counter() - t0
 
-    S0 = 8
+    # size the sample from a 64-row probe; the whole step (all M rows) is the
+    # cap -- on a 16-core host the full step takes a few seconds
+    S0 = 64
     t = step(S0)
     S = int(max(S0, min(up.M, S0 * seconds / max(t, 1e-6))))
     t = step(S)
@@ -169,6 +243,9 @@ def sweep(args, torch, w8, synthetic):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
               f"(the layer shards over tokens or output channels without communication; see the "
@@ -184,6 +261,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
     if args.sweep:
         sweep(args, torch, w8, synthetic)
         return 0
