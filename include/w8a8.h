@@ -70,7 +70,10 @@ const char* w8a8_status_string(int status);
  * Per-token activation quantization.
  *   x      bf16 [M, K], row stride ldx elements (ldx >= K, ldx % 8 == 0)
  *   q      int8 [M, K] out, row stride ldq (ldq >= K, ldq % 16 == 0)
- *   scale  fp32 [M] out: scale[m] = absmax(x[m, :]) / 127
+ *   scale  fp32 [M] out: scale[m] = absmax(x[m, :]) / 127 (IEEE fp32)
+ *   q[m,k] = clamp(round_half_even(fp32(x[m,k] / scale[m])), -127, 127),
+ *   all zero where scale[m] == 0.  Inputs must be finite; rows holding NaN
+ *   or Inf get unspecified codes.
  * Source: the Abstract's per-token activation quantization.
  */
 int w8a8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
@@ -136,7 +139,10 @@ int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w,
  * GELU followed by per-token quantization, for the activation between the
  * two linears of a DiT MLP (not on the pages; part of the DiT MLP workload):
  *   h[m,k] = bf16_rne(gelu(y[m,k])),  gelu(v) = 0.5 * v * erfc(-v / sqrt(2))
+ *   correctly rounded (one rounding of the exact value; the kernel looks it
+ *   up in a 65536-entry table of bf16 results built in double precision),
  *   then q, scale from h exactly as w8a8_quantize_act.
+ *   Inputs must be finite; rows holding NaN or Inf get unspecified codes.
  *   y      bf16 [M, K], row stride ldy (ldy >= K, ldy % 8 == 0)
  *   q      int8 [M, K] out (row stride ldq), scale fp32 [M] out
  *   h_out  bf16 [M, K] out (row stride K) or NULL: the GELU values that were

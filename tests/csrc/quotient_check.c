@@ -1,0 +1,55 @@
+/* Exhaustive check of the reciprocal-based quotient used by the bf16
+ * quantization kernels.
+ *
+ * For every positive finite bf16 absmax a and every bf16 x with 0 <= x <= a
+ * (the sign is symmetric), with s = fl32(a / 127) and, when s >= 2^-96,
+ * r = fl32(1 / s), q = fl32(x * r), q' = fma(fma(-q, s, x), r, q):
+ *   clamp(rne(q'), -127, 127) == clamp(rne(fl32(x / s)), -127, 127).
+ * Also checks that adding 1.5 * 2^23 to the clamped quotient rounds it to the
+ * same integer as rint(), with that integer's two's-complement byte in the
+ * low byte of the sum's bit pattern.
+ * Prints "pairs N mismatches M" and exits 0 iff M == 0.  Compile with
+ * -O2 -ffp-contract=off -fopenmp (fmaf must be the fused operation). */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+static float bf16(uint32_t b) {
+  uint32_t u = b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static uint32_t bits(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+int main(void) {
+  long long pairs = 0, bad = 0;
+  const float min_scale = 0x1p-96f;
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, bad)
+  for (int a = 1; a < 0x7F80; ++a) {
+    const float amax = bf16((uint32_t)a);
+    const float s = amax / 127.0f;
+    if (!(s >= min_scale)) continue;
+    const float r = 1.0f / s;
+    for (int xb = 0; xb <= a; ++xb) {
+      const float x = bf16((uint32_t)xb);
+      float want = rintf(x / s);
+      want = fminf(fmaxf(want, -127.0f), 127.0f);
+      const float q = x * r;
+      float t = fmaf(fmaf(-q, s, x), r, q);
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+      const uint32_t w = bits(t + 12582912.0f);
+      const int code = (int)(int8_t)(w & 0xFFu);
+      ++pairs;
+      if ((float)code != want || rintf(t) != want) ++bad;
+    }
+  }
+  printf("pairs %lld mismatches %lld\n", pairs, bad);
+  return bad == 0 ? 0 : 1;
+}

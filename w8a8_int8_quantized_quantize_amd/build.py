@@ -6,6 +6,9 @@ Flags that the numerical contract depends on:
   -fno-gpu-flush-denormals-to-zero         fp32 denormals kept
 Packed fp32 instructions are disabled (-packed-fp32-ops); the host pass warns
 that it does not know that feature, which is harmless.
+
+The GELU table compiled into quantize.hip is written first, into the build
+folder, by csrc/gen_gelu_lut.py.
 """
 from __future__ import annotations
 
@@ -30,7 +33,7 @@ COMMON = [
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-command-line-argument",
+    "-I", INCLUDE, "-I", CSRC, "-I", BUILD, "-Wall", "-Wno-unused-command-line-argument",
 ]
 
 
@@ -53,6 +56,10 @@ def build(save_temps: bool | None = None) -> str:
     if save_temps is None:
         save_temps = os.environ.get("W8A8_SAVE_TEMPS", "0") == "1"
     os.makedirs(BUILD, exist_ok=True)
+    r = subprocess.run([sys.executable, os.path.join(CSRC, "gen_gelu_lut.py"),
+                        os.path.join(BUILD, "gelu_lut.inc")], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("gen_gelu_lut.py failed:\n" + r.stderr)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()

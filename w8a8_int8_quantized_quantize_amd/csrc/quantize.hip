@@ -11,9 +11,29 @@
 // Design: one 64-lane wavefront per row.  Each lane loads 16-byte chunks
 // strided by 64 chunks (fully coalesced 1 KiB per wave instruction), keeps
 // them in registers, reduces |x| to the row maximum with cross-lane shuffles,
-// then divides, rounds and packs the codes into 8-byte (bf16 input) or 4-byte
+// then computes the codes and packs them into 8-byte (bf16 input) or 4-byte
 // (fp32 input) coalesced stores.  The row is read from HBM exactly once.  Rows
 // too long for the register budget take a two-pass loop (second read from L2).
+//
+// bf16 rows never leave their packed form until the code is computed: the
+// absmax is a packed 16-bit integer max of the magnitude bits (the order of
+// non-negative bf16 patterns is the order of their values).
+//
+// Quotient x / scale, bf16 rows: with r = fl32(1 / s) (one IEEE division per
+// row), q = fl32(x * r), e = fma(-q, s, x) (exact) and q' = fma(e, r, q),
+// q' = fl32(x / s) -- Markstein's correction of a reciprocal-based quotient.
+// It is used for rows with s >= 2^-96, where an exhaustive check over every
+// pair of bf16 values |x| <= absmax confirms it (the residual e stays in the
+// normal range there); smaller scales, and fp32 rows, use the IEEE division.
+// Rounding: clamp to [-127, 127] (v_med3), then adding 1.5 * 2^23 rounds to
+// an integer, half to even, whose two's-complement byte is the low byte of the
+// sum's bit pattern.
+//
+// GELU: the input is bf16, so gelu is a function on 65536 patterns; its
+// correctly rounded bf16 values form a 128 KiB table (written at build time by
+// gen_gelu_lut.py in double precision) that every workgroup stages in LDS
+// with direct-to-LDS loads.  One workgroup of 16 waves per CU (the table fills
+// 128 KiB of the 160 KiB of LDS); each element then costs one LDS gather.
 //
 // Exactness: built with correctly rounded fp32 division, fp32 denormals kept
 // and contraction off, so every step matches the IEEE definition bit for bit.
@@ -22,9 +42,26 @@
 namespace w8a8 {
 namespace {
 
-constexpr int kWaves = 4;                 // rows per workgroup
+constexpr int kWaves = 4;                 // rows per workgroup (plain kernels)
 constexpr int kThreads = 64 * kWaves;
 constexpr int64_t kMaxBlocks = 1 << 20;   // grid cap; rows are grid-strided
+constexpr int kLutWaves = 16;             // GELU kernels: one workgroup per CU
+constexpr int kLutThreads = 64 * kLutWaves;
+constexpr int kLutMaxBlocks = 256;        // persistent: one per compute unit
+constexpr float kFastMinScale = 0x1p-96f;
+
+__device__ const uint16_t kGeluLut[65536] __attribute__((aligned(16))) = {
+#include "gelu_lut.inc"
+};
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wave index within the workgroup, in a scalar register (so row bases are
+// scalar and per-lane addresses are 32-bit offsets from them).
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -32,173 +69,434 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ float gelu_bf16(float v) {
-  // 0.5 * v * erfc(-v / sqrt(2)); the erfc form keeps relative accuracy in
-  // the negative tail, where 1 + erf(.) cancels.
-  const float g = 0.5f * v * erfcf(-v * 0.70710678118654752f);
-  return static_cast<float>(static_cast<__bf16>(g));  // RNE to bf16
+// Packed |x| max of two bf16 values per 32-bit word.
+__device__ __forceinline__ u16x2 absmax2(u16x2 m, uint32_t w) {
+  const uint32_t a = w & 0x7FFF7FFFu;
+  return __builtin_elementwise_max(m, *reinterpret_cast<const u16x2*>(&a));
 }
 
-__device__ __forceinline__ uint32_t quant_code(float x, float s) {
-  const float t = x / s;                               // one IEEE division
-  float r = __builtin_rintf(t);                        // half to even
-  r = __builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f);
-  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+__device__ __forceinline__ float absmax_of(u16x2 m) {
+  const uint32_t b = m.x > m.y ? m.x : m.y;
+  return __uint_as_float(b << 16);
 }
 
-template <QuantSrc SRC>
-struct Src {
-  static constexpr bool kF32 = (SRC == QuantSrc::kF32);
-  static constexpr bool kGelu = (SRC == QuantSrc::kBf16Gelu);
-  static constexpr int kEpc = kF32 ? 4 : 8;  // elements per 16-byte chunk
-  static constexpr int kElemBytes = kF32 ? 4 : 2;
+// Element c of a row through a 32-bit byte offset from the row's (scalar)
+// base, which lets the compiler use the scalar-base + vector-offset form.
+template <typename T>
+__device__ __forceinline__ T& at(T* base, uint32_t c) {
+  return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + c * static_cast<uint32_t>(sizeof(T)));
+}
+template <typename T>
+__device__ __forceinline__ const T& at(const T* base, uint32_t c) {
+  return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) +
+                                     c * static_cast<uint32_t>(sizeof(T)));
+}
 
-  // Unpack one 16-byte chunk into kEpc floats (GELU applied if requested).
-  static __device__ __forceinline__ void unpack(const uint4 raw, float* v) {
-    if constexpr (kF32) {
-      v[0] = __uint_as_float(raw.x);
-      v[1] = __uint_as_float(raw.y);
-      v[2] = __uint_as_float(raw.z);
-      v[3] = __uint_as_float(raw.w);
-    } else {
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+// Loads the CH chunks of a row as exactly CH unconditional load
+// instructions: chunk indices past the row's end are clamped to its last
+// chunk, so those registers hold a copy of real elements (harmless for the
+// absmax; their codes are never stored).  Requires nch > 0.
+template <int CH>
+__device__ __forceinline__ void load_row(const uint4* src, uint32_t nch, uint32_t ln,
+                                         uint4 (&raw)[CH]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-      if constexpr (kGelu) {
+  for (int j = 0; j < CH; ++j) {
+    const uint32_t c = ln + 64u * j;
+    raw[j] = at(src, c < nch ? c : nch - 1);
+    __builtin_amdgcn_sched_barrier(0);  // issue order = chunk order
+  }
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Code of x as the low byte of the returned word.  MODE 0: s == 0 (all
+// zero); MODE 1: IEEE division; MODE 2: reciprocal + Markstein correction.
+template <int MODE>
+__device__ __forceinline__ uint32_t code_word(float x, float s, float r) {
+  float t;
+  if constexpr (MODE == 0) {
+    return 0u;
+  } else if constexpr (MODE == 1) {
+    t = x / s;
+  } else {
+    const float q = x * r;
+    t = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+  }
+  t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
+  return __float_as_uint(t + 12582912.0f);
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+template <int MODE>
+__device__ __forceinline__ uint2 codes_bf16x8(const uint4 raw, float s, float r) {
+  uint2 p;
+  p.x = pack4(code_word<MODE>(bf_lo(raw.x), s, r), code_word<MODE>(bf_hi(raw.x), s, r),
+              code_word<MODE>(bf_lo(raw.y), s, r), code_word<MODE>(bf_hi(raw.y), s, r));
+  p.y = pack4(code_word<MODE>(bf_lo(raw.z), s, r), code_word<MODE>(bf_hi(raw.z), s, r),
+              code_word<MODE>(bf_lo(raw.w), s, r), code_word<MODE>(bf_hi(raw.w), s, r));
+  return p;
+}
+
+__device__ __forceinline__ uint32_t codes_f32x4(const uint4 raw, float s) {
+  if (s == 0.0f) return 0u;
+  return pack4(code_word<1>(__uint_as_float(raw.x), s, 0.f), code_word<1>(__uint_as_float(raw.y), s, 0.f),
+               code_word<1>(__uint_as_float(raw.z), s, 0.f), code_word<1>(__uint_as_float(raw.w), s, 0.f));
+}
+
+// Scale of a bf16 row from its packed absmax; returns the quotient mode.
+__device__ __forceinline__ int row_scale(u16x2 m, float& s, float& r) {
+  s = wave_max(absmax_of(m)) / 127.0f;
+  if (s == 0.0f) return 0;
+  if (s >= kFastMinScale) {
+    r = 1.0f / s;
+    return 2;
+  }
+  return 1;
+}
+
+// Quantize CH register-held bf16 chunks of one row (chunk j is c = lane+64j).
+template <int CH>
+__device__ __forceinline__ void emit_bf16_row(const uint4 (&raw)[CH], int mode, float s, float r,
+                                              uint32_t nch, uint32_t ln, int8_t* qrow) {
+  uint2* dst = reinterpret_cast<uint2*>(qrow);
+  if (mode == 2) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = gelu_bf16(v[i]);
-      }
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t c = ln + 64u * j;
+      if (c < nch) at(dst, c) = codes_bf16x8<2>(raw[j], s, r);
+    }
+  } else if (mode == 1) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t c = ln + 64u * j;
+      if (c < nch) at(dst, c) = codes_bf16x8<1>(raw[j], s, r);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t c = ln + 64u * j;
+      if (c < nch) at(dst, c) = make_uint2(0u, 0u);
     }
   }
+}
 
-  // Quantize one chunk and store its codes (and, for GELU, its bf16 values).
-  static __device__ __forceinline__ void emit(const float* v, float s, int8_t* qrow,
-                                              uint16_t* hrow, int64_t c) {
-    uint32_t code[kEpc];
+// ------------------------------------------------------------ bf16 rows --
+template <int CH>
+__global__ __launch_bounds__(kThreads) void quantize_bf16_regs(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave_id(); row < M;
+       row += (int64_t)gridDim.x * kWaves) {
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    uint4 raw[CH];
+    load_row<CH>(reinterpret_cast<const uint4*>(x + row * ldx), nch, ln, raw);
+    u16x2 m = {0, 0};
 #pragma unroll
-    for (int i = 0; i < kEpc; ++i) code[i] = (s == 0.0f) ? 0u : quant_code(v[i], s);
-    if constexpr (kF32) {
-      const uint32_t p = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-      *reinterpret_cast<uint32_t*>(qrow + c * 4) = p;
-    } else {
-      uint2 p;
-      p.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-      p.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-      *reinterpret_cast<uint2*>(qrow + c * 8) = p;
-      if constexpr (kGelu) {
-        if (hrow != nullptr) {
-          uint4 h;
-          uint32_t hw[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            hw[i] = (__float_as_uint(v[2 * i]) >> 16) | (__float_as_uint(v[2 * i + 1]) & 0xFFFF0000u);
-          h.x = hw[0]; h.y = hw[1]; h.z = hw[2]; h.w = hw[3];
-          *reinterpret_cast<uint4*>(hrow + c * 8) = h;
-        }
-      }
+    for (int j = 0; j < CH; ++j)
+      m = absmax2(absmax2(absmax2(absmax2(m, raw[j].x), raw[j].y), raw[j].z), raw[j].w);
+    float s, r = 0.0f;
+    const int mode = row_scale(m, s, r);
+    if (lane == 0) scale[row] = s;
+    emit_bf16_row<CH>(raw, mode, s, r, nch, ln, q + row * ldq);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_bf16_loop(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave_id(); row < M;
+       row += (int64_t)gridDim.x * kWaves) {
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx);
+    u16x2 m = {0, 0};
+    for (uint32_t c = ln; c < nch; c += 64) {
+      const uint4 v = at(src, c);
+      m = absmax2(absmax2(absmax2(absmax2(m, v.x), v.y), v.z), v.w);
     }
+    float s, r = 0.0f;
+    const int mode = row_scale(m, s, r);
+    if (lane == 0) scale[row] = s;
+    uint2* dst = reinterpret_cast<uint2*>(q + row * ldq);
+    for (uint32_t c = ln; c < nch; c += 64) {
+      const uint4 v = at(src, c);
+      at(dst, c) = mode == 2 ? codes_bf16x8<2>(v, s, r)
+                         : (mode == 1 ? codes_bf16x8<1>(v, s, r) : make_uint2(0u, 0u));
+    }
+  }
+}
+
+// ----------------------------------------------------------- GELU rows --
+// GELU of 8 packed bf16 values through the table: issue() starts the 8
+// gathers, pack() joins the halves.  The packed words are made opaque: the
+// compiler would otherwise keep the 16-bit halves apart until their use,
+// doubling the registers a register-held row needs.
+struct Gather8 {
+  uint32_t h[8];
+  __device__ __forceinline__ void issue(const uint16_t* lut, const uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = lut[w[i] & 0xFFFFu];
+      h[2 * i + 1] = lut[w[i] >> 16];
+    }
+  }
+  __device__ __forceinline__ uint4 pack() const {
+    uint4 p = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                         h[6] | (h[7] << 16));
+    asm volatile("" : "+v"(p.x), "+v"(p.y), "+v"(p.z), "+v"(p.w));
+    return p;
   }
 };
 
-// CH > 0: each lane holds CH chunks of the row in registers (one HBM read).
-template <QuantSrc SRC, int CH>
-__global__ __launch_bounds__(kThreads) void quantize_rows_regs(
-    const void* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
-  using S = Src<SRC>;
-  const int lane = threadIdx.x & 63;
-  const int64_t nch = K / S::kEpc;
-  for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < M;
-       row += (int64_t)gridDim.x * kWaves) {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) +
-                                                      row * ldx * S::kElemBytes);
-    float v[CH][S::kEpc];
-    float amax = 0.0f;
+__device__ __forceinline__ uint4 gelu_chunk(const uint16_t* lut, uint4 v) {
+  Gather8 g;
+  g.issue(lut, v);
+  return g.pack();
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit field");
+  // gfx9 s_waitcnt: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt
+  // (bits 6:4) and lgkmcnt (bits 11:8) left at their maxima (no wait).
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Stage the table: 8192 16-byte pieces, 8 per lane, straight into LDS.
+__device__ __forceinline__ void stage_lut(uint16_t* lut) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8192 / kLutThreads; ++i) {
+    const int piece = (i * kLutWaves + wave) * 64;  // first piece of this wave instruction
+    const uint16_t* g = kGeluLut + (piece + lane) * 8;
+    lds_void* d = (lds_void*)(lut + piece * 8);
+    __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
+  }
+}
+
+// GELU through the staged table, absmax, optional h copy, codes.
+template <int CH>
+__device__ __forceinline__ void gelu_finish_row(const uint16_t* lut, uint4 (&raw)[CH], int64_t row,
+                                                int64_t K, uint32_t nch, uint32_t ln, int lane,
+                                                int8_t* q, int64_t ldq, float* scale,
+                                                uint16_t* h_out) {
+  u16x2 m = {0, 0};
+  Gather8 cur;
+  cur.issue(lut, raw[0]);
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    Gather8 nxt;
+    if (j + 1 < CH) nxt.issue(lut, raw[j + 1]);  // next chunk's gathers in flight
+    raw[j] = cur.pack();
+    m = absmax2(absmax2(absmax2(absmax2(m, raw[j].x), raw[j].y), raw[j].z), raw[j].w);
+    cur = nxt;
+    __builtin_amdgcn_sched_barrier(0);  // at most two chunks' gathers at a time
+  }
+  if (h_out != nullptr) {
+    uint4* hrow = reinterpret_cast<uint4*>(h_out + row * K);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int64_t c = lane + 64 * j;
-      uint4 raw = make_uint4(0u, 0u, 0u, 0u);
-      if (c < nch) raw = src[c];
-      S::unpack(raw, v[j]);
-#pragma unroll
-      for (int i = 0; i < S::kEpc; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+      const uint32_t c = ln + 64u * j;
+      if (c < nch) at(hrow, c) = raw[j];
     }
-    amax = wave_max(amax);
-    const float s = amax / 127.0f;
-    if (lane == 0) scale[row] = s;
-    int8_t* qrow = q + row * ldq;
-    uint16_t* hrow = h_out ? h_out + row * K : nullptr;
+  }
+  float s, r = 0.0f;
+  const int mode = row_scale(m, s, r);
+  if (lane == 0) scale[row] = s;
+  emit_bf16_row<CH>(raw, mode, s, r, nch, ln, q + row * ldq);
+}
+
+template <int CH>
+__global__ __launch_bounds__(kLutThreads) void gelu_quantize_regs(
+    const uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t ldy, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lut[65536];
+  const int lane = threadIdx.x & 63;
+  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  const int64_t stride = (int64_t)gridDim.x * kLutWaves;
+  int64_t row = (int64_t)blockIdx.x * kLutWaves + wave_id();
+  stage_lut(lut);
+  // First row, peeled: its loads go out while the table pieces are in
+  // flight.  Every wave reaches a barrier, also one without a row.
+  if (row < M && nch > 0) {
+    uint4 raw[CH];
+    __builtin_amdgcn_sched_barrier(0);
+    load_row<CH>(reinterpret_cast<const uint4*>(y + row * ldy), nch, lane, raw);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<CH>();   // loads complete in order: the older table pieces have landed
+    __builtin_amdgcn_s_barrier();  // ... and so have every other wave's
+    __builtin_amdgcn_sched_barrier(0);
+    gelu_finish_row<CH>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
+  } else {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    if (row >= M) return;
+    uint4 raw[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int64_t c = lane + 64 * j;
-      if (c < nch) S::emit(v[j], s, qrow, hrow, c);
+    for (int j = 0; j < CH; ++j) raw[j] = make_uint4(0u, 0u, 0u, 0u);
+    gelu_finish_row<CH>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
+  }
+  for (row += stride; row < M; row += stride) {
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    uint4 raw[CH];
+    load_row<CH>(reinterpret_cast<const uint4*>(y + row * ldy), nch, ln, raw);
+    gelu_finish_row<CH>(lut, raw, row, K, nch, ln, lane, q, ldq, scale, h_out);
+  }
+}
+
+__global__ __launch_bounds__(kLutThreads) void gelu_quantize_loop(
+    const uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t ldy, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lut[65536];
+  const int lane = threadIdx.x & 63;
+  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  stage_lut(lut);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  for (int64_t row = (int64_t)blockIdx.x * kLutWaves + wave_id(); row < M;
+       row += (int64_t)gridDim.x * kLutWaves) {
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    const uint4* src = reinterpret_cast<const uint4*>(y + row * ldy);
+    u16x2 m = {0, 0};
+    for (uint32_t c = ln; c < nch; c += 64) {
+      const uint4 v = gelu_chunk(lut, at(src, c));
+      m = absmax2(absmax2(absmax2(absmax2(m, v.x), v.y), v.z), v.w);
+    }
+    float s, r = 0.0f;
+    const int mode = row_scale(m, s, r);
+    if (lane == 0) scale[row] = s;
+    uint2* dst = reinterpret_cast<uint2*>(q + row * ldq);
+    uint4* hrow = h_out ? reinterpret_cast<uint4*>(h_out + row * K) : nullptr;
+    for (uint32_t c = ln; c < nch; c += 64) {
+      const uint4 v = gelu_chunk(lut, at(src, c));
+      if (hrow != nullptr) at(hrow, c) = v;
+      at(dst, c) = mode == 2 ? codes_bf16x8<2>(v, s, r)
+                         : (mode == 1 ? codes_bf16x8<1>(v, s, r) : make_uint2(0u, 0u));
     }
   }
 }
 
-// Rows longer than the register budget: pass 1 finds the absmax, pass 2
-// re-reads (mostly from L2) and quantizes.  GELU is recomputed identically.
-template <QuantSrc SRC>
-__global__ __launch_bounds__(kThreads) void quantize_rows_loop(
-    const void* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
-  using S = Src<SRC>;
+// ------------------------------------------------------------ fp32 rows --
+__device__ __forceinline__ float absmax4(float m, const uint4 v) {
+  m = fmaxf(m, fabsf(__uint_as_float(v.x)));
+  m = fmaxf(m, fabsf(__uint_as_float(v.y)));
+  m = fmaxf(m, fabsf(__uint_as_float(v.z)));
+  return fmaxf(m, fabsf(__uint_as_float(v.w)));
+}
+
+template <int CH>
+__global__ __launch_bounds__(kThreads) void quantize_f32_regs(
+    const float* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
-  const int64_t nch = K / S::kEpc;
-  for (int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6); row < M;
+  const uint32_t nch = static_cast<uint32_t>(K / 4);
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave_id(); row < M;
        row += (int64_t)gridDim.x * kWaves) {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(x) +
-                                                      row * ldx * S::kElemBytes);
-    float amax = 0.0f;
-    for (int64_t c = lane; c < nch; c += 64) {
-      float v[S::kEpc];
-      S::unpack(src[c], v);
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    uint4 raw[CH];
+    load_row<CH>(reinterpret_cast<const uint4*>(x + row * ldx), nch, ln, raw);
+    float m = 0.0f;
 #pragma unroll
-      for (int i = 0; i < S::kEpc; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    }
-    amax = wave_max(amax);
-    const float s = amax / 127.0f;
+    for (int j = 0; j < CH; ++j) m = absmax4(m, raw[j]);
+    const float s = wave_max(m) / 127.0f;
     if (lane == 0) scale[row] = s;
-    int8_t* qrow = q + row * ldq;
-    uint16_t* hrow = h_out ? h_out + row * K : nullptr;
-    for (int64_t c = lane; c < nch; c += 64) {
-      float v[S::kEpc];
-      S::unpack(src[c], v);
-      S::emit(v, s, qrow, hrow, c);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * ldq);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t c = ln + 64u * j;
+      if (c < nch) at(dst, c) = codes_f32x4(raw[j], s);
     }
   }
 }
 
-template <QuantSrc SRC>
-hipError_t launch_src(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
-                      float* scale, uint16_t* h_out, hipStream_t stream) {
-  constexpr int kEpc = Src<SRC>::kEpc;
-  const int64_t per_lane = (K / kEpc + 63) / 64;
-  int64_t blocks = (M + kWaves - 1) / kWaves;
-  if (blocks > kMaxBlocks) blocks = kMaxBlocks;
+__global__ __launch_bounds__(kThreads) void quantize_f32_loop(
+    const float* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t nch = static_cast<uint32_t>(K / 4);
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave_id(); row < M;
+       row += (int64_t)gridDim.x * kWaves) {
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx);
+    float m = 0.0f;
+    for (uint32_t c = ln; c < nch; c += 64) m = absmax4(m, at(src, c));
+    const float s = wave_max(m) / 127.0f;
+    if (lane == 0) scale[row] = s;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * ldq);
+    for (uint32_t c = ln; c < nch; c += 64) at(dst, c) = codes_f32x4(at(src, c), s);
+  }
+}
+
+// --------------------------------------------------------------- launch --
+// Register-held chunk counts per lane; longer rows, and K == 0 (scales 0,
+// no loads), take the loop kernels.
+#define W8A8_FOR_CH(X) X(1) X(2) X(3) X(4) X(6) X(8) X(12) X(16) X(24)
+
+hipError_t launch_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                       int64_t ldq, float* scale, hipStream_t stream) {
+  const int64_t per_lane = (K / 8 + 63) / 64;
+  const int64_t blocks = std::min<int64_t>((M + kWaves - 1) / kWaves, kMaxBlocks);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
 #define W8A8_Q_CASE(CHV)                                                                  \
-  if (per_lane <= CHV) {                                                                  \
-    quantize_rows_regs<SRC, CHV><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale, \
-                                                             h_out);                      \
+  if (K > 0 && per_lane <= CHV) {                                                                  \
+    quantize_bf16_regs<CHV><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);     \
     return hipGetLastError();                                                             \
   }
-  W8A8_Q_CASE(1)
-  W8A8_Q_CASE(2)
-  W8A8_Q_CASE(3)
-  W8A8_Q_CASE(4)
-  W8A8_Q_CASE(6)
-  W8A8_Q_CASE(8)
-  W8A8_Q_CASE(12)
-  W8A8_Q_CASE(16)
-  W8A8_Q_CASE(24)
+  W8A8_FOR_CH(W8A8_Q_CASE)
 #undef W8A8_Q_CASE
-  quantize_rows_loop<SRC><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale, h_out);
+  quantize_bf16_loop<<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
   return hipGetLastError();
 }
+
+hipError_t launch_gelu(const uint16_t* y, int64_t M, int64_t K, int64_t ldy, int8_t* q,
+                       int64_t ldq, float* scale, uint16_t* h_out, hipStream_t stream) {
+  const int64_t per_lane = (K / 8 + 63) / 64;
+  const int64_t blocks = std::min<int64_t>((M + kLutWaves - 1) / kLutWaves, kLutMaxBlocks);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kLutThreads);
+#define W8A8_G_CASE(CHV)                                                                     \
+  if (K > 0 && per_lane <= CHV) {                                                                     \
+    gelu_quantize_regs<CHV><<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out); \
+    return hipGetLastError();                                                                \
+  }
+  W8A8_FOR_CH(W8A8_G_CASE)
+#undef W8A8_G_CASE
+  gelu_quantize_loop<<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_f32(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
+                      float* scale, hipStream_t stream) {
+  const int64_t per_lane = (K / 4 + 63) / 64;
+  const int64_t blocks = std::min<int64_t>((M + kWaves - 1) / kWaves, kMaxBlocks);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+#define W8A8_F_CASE(CHV)                                                                  \
+  if (K > 0 && per_lane <= CHV) {                                                                  \
+    quantize_f32_regs<CHV><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);      \
+    return hipGetLastError();                                                             \
+  }
+  W8A8_FOR_CH(W8A8_F_CASE)
+#undef W8A8_F_CASE
+  quantize_f32_loop<<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
+  return hipGetLastError();
+}
+
+#undef W8A8_FOR_CH
 
 }  // namespace
 
@@ -207,11 +505,12 @@ hipError_t launch_quantize_rows(QuantSrc src, const void* x, int64_t M, int64_t 
                                 hipStream_t stream) {
   switch (src) {
     case QuantSrc::kBf16:
-      return launch_src<QuantSrc::kBf16>(x, M, K, ldx, q, ldq, scale, nullptr, stream);
+      return launch_bf16(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, stream);
     case QuantSrc::kF32:
-      return launch_src<QuantSrc::kF32>(x, M, K, ldx, q, ldq, scale, nullptr, stream);
+      return launch_f32(static_cast<const float*>(x), M, K, ldx, q, ldq, scale, stream);
     case QuantSrc::kBf16Gelu:
-      return launch_src<QuantSrc::kBf16Gelu>(x, M, K, ldx, q, ldq, scale, h_out, stream);
+      return launch_gelu(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, h_out,
+                         stream);
   }
   return hipErrorInvalidValue;
 }
