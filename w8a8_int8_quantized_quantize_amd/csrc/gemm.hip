@@ -38,6 +38,8 @@
 // 16 (API contract), so a chunk is entirely inside or outside K.
 #include "internal.h"
 
+#include <type_traits>
+
 namespace w8a8 {
 namespace {
 
@@ -101,6 +103,9 @@ struct Tile {
   static constexpr int kLoads = (BM + BN) / kRowsPerLoad;  // per stage, whole workgroup
   static constexpr int kLoadsPerWave = (kLoads + kWaves - 1) / kWaves;
   static constexpr int kStage = (BM + BN) * BK;     // LDS bytes per stage
+  // 3+ stages: refill loads are spread over the stage after the one whose
+  // buffer they refill (one slice per MFMA row)
+  static constexpr bool kSpread = STAGES >= 3;
   static_assert(BK == 64 || BK == 128, "BK");
   static_assert(kSteps >= 2 && kSteps % 2 == 0, "fragment sets alternate within a stage");
   static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be whole MFMA blocks");
@@ -207,14 +212,18 @@ struct Loader {
     lane_off = static_cast<uint32_t>(lr * K + swz<C::kSlots>(rbase + lr, p) * 16);
   }
 
-  int koff = 0, kst = 1;  // K-stage rotation (see run_tile)
 
   __device__ __forceinline__ void issue(int s, int8_t* dst, int wave, int lane) const {
-    int ks = s + koff;
-    if (ks >= kst) ks -= kst;
-    const int64_t k0 = static_cast<int64_t>(ks) * C::BK;
+    issue_part<0, C::kLoadsPerWave>(s, dst, wave, lane);
+  }
+
+  // This wave's loads [J0, J1) of stage s.
+  template <int J0, int J1>
+  __device__ __forceinline__ void issue_part(int s, int8_t* dst, int wave, int lane) const {
+    if constexpr (J0 >= J1) return;
+    const int64_t k0 = static_cast<int64_t>(s) * C::BK;
 #pragma unroll
-    for (int jj = 0; jj < C::kLoadsPerWave; ++jj) {
+    for (int jj = J0; jj < J1; ++jj) {
       const int j = wave + jj * C::kWaves;
       if (C::kLoads % C::kWaves != 0 && j >= C::kLoads) break;
       const bool is_w = jj < kWBlocksPerWave;  // compile-time after unrolling
@@ -252,10 +261,11 @@ __device__ __forceinline__ void read_frags(Frags<C>& fr, const int8_t* stage, ui
                                            uint32_t lx) {
   const int8_t* sw = stage + lw;
   const int8_t* sx = stage + lx;
-#pragma unroll
-  for (int f = 0; f < C::FN; ++f) fr.w[f] = *reinterpret_cast<const v4i*>(sw + f * C::MF * C::BK);
+  // same order as the interleaved schedule: activation fragments first
 #pragma unroll
   for (int f = 0; f < C::FM; ++f) fr.x[f] = *reinterpret_cast<const v4i*>(sx + f * C::MF * C::BK);
+#pragma unroll
+  for (int f = 0; f < C::FN; ++f) fr.w[f] = *reinterpret_cast<const v4i*>(sw + f * C::MF * C::BK);
 }
 
 // MFMAs of one k-step, weight-fragment rows [I0, I1).
@@ -489,10 +499,140 @@ __device__ __forceinline__ void zero_tail(Frags<C>& fr, int64_t kstep0, int64_t 
   }
 }
 
+// Wait for the next stage's loads (this wave's) at the end of a stage.
+// `ahead` whole later stages may stay in flight; with spread refills the
+// last of them is only partly issued at this point.
+template <class C, bool REFILL>
+__device__ __forceinline__ void wait_next_stage(int ahead) {
+  if constexpr (C::kSpread && REFILL) {
+    // after stage st + 1's loads: stages st + 2 .. st + S - 2 whole, and the
+    // part of stage st + S - 1 issued in this stage's earlier k-steps
+    constexpr int L = C::kLoadsPerWave;
+    constexpr int P = L * (C::kSteps - 1) / C::kSteps;
+    wait_vm<(C::STAGES - 3) * L + P>();
+  } else {
+    wait_stages<C>(ahead);
+  }
+}
+
+// Interleaved k-step schedule.  A k-step is FN x FM MFMAs, row-major (row i
+// uses weight fragment i with every activation fragment).  Its fragments are
+// read during the previous k-step, one ds_read_b128 at a time between MFMAs,
+// in the order x[0..FM-1], w[0..FN-1]; the refill loads go out one slice per
+// row.  Issuing LDS reads and loads in bursts stalls the issuing wave (the
+// LDS and address queues fill up) and, with one wave per SIMD, the matrix
+// core with it; spread out, they overlap the MFMAs.
+//   * a k-step that is not the last of its stage issues the next k-step's
+//     reads over its first half, so they have all landed when the stage ends;
+//   * the last k-step opens the next stage (wait for its loads, barrier) and
+//     issues the next stage's first reads over its first three quarters, so
+//     they have landed when the next stage starts.
+template <class C>
+struct Sched {
+  static constexpr int R = C::FM + C::FN;  // fragment reads per k-step
+  static constexpr int NM = C::FN * C::FM; // MFMAs per k-step
+  // MFMA index after which read r is issued
+  static constexpr int read_after(bool last, int r) {
+    return last ? r * (3 * NM / 4 > 0 ? 3 * NM / 4 : 1) / R : r * (NM / 2 > 0 ? NM / 2 : 1) / R;
+  }
+  // reads of a `last`-type schedule issued before MFMA index j
+  static constexpr int reads_before(bool last, int j) {
+    int n = 0;
+    for (int r = 0; r < R; ++r) n += read_after(last, r) < j ? 1 : 0;
+    return n;
+  }
+  // lgkmcnt that guarantees row i's fragments (x[0..FM-1], w[i]) of a
+  // non-last k-step have landed: the reads issued after w[i] (rest of the
+  // previous step's reads, then this step's reads so far) may stay pending
+  static constexpr int row_wait(int i) {
+    const int n = (R - 1 - (C::FM + i)) + reads_before(false, i * C::FM);
+    return n > 15 ? 15 : n;
+  }
+  // MFMA index after which the refill slice of row i goes out
+  static constexpr int dma_after(int i) { return i * C::FM + (C::FM - 1) / 2; }
+};
+
+template <class C>
+__device__ __forceinline__ void read_frag(Frags<C>& fr, int r, const int8_t* stage, uint32_t lw,
+                                          uint32_t lx) {
+  if (r < C::FM)
+    fr.x[r] = *reinterpret_cast<const v4i*>(stage + lx + r * C::MF * C::BK);
+  else
+    fr.w[r - C::FM] = *reinterpret_cast<const v4i*>(stage + lw + (r - C::FM) * C::MF * C::BK);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm<63, N>());
+}
+
+// MFMAs J.. of k-step KS with the reads of the following k-step (into fn,
+// from stage `rstage`) and the refill slices woven in.
+template <class C, bool FAST, bool REFILL, int KS, int J>
+__device__ __forceinline__ void step_mfmas(const Loader<C, FAST>& ld, const Frags<C>& fc,
+                                           Frags<C>& fn, typename C::Acc (&acc)[C::FN][C::FM],
+                                           const int8_t* rstage, uint32_t rlw, uint32_t rlx, int rs,
+                                           int8_t* rbuf, int wave, int lane) {
+  using Sc = Sched<C>;
+  constexpr bool LAST = KS + 1 == C::kSteps;
+  if constexpr (J < Sc::NM) {
+    constexpr int i = J / C::FM, jj = J % C::FM;
+    if constexpr (!LAST && jj == 0) wait_lgkm<Sc::row_wait(i)>();  // row i's fragments landed
+    sched_fence();
+    acc[i][jj] = C::Op::run(fc.w[i], fc.x[jj], acc[i][jj]);
+    sched_fence();
+#pragma unroll
+    for (int r = 0; r < Sc::R; ++r)
+      if (Sc::read_after(LAST, r) == J) read_frag<C>(fn, r, rstage, rlw, rlx);
+    if constexpr (REFILL) {
+      if constexpr (C::kSpread) {
+        if constexpr (Sc::dma_after(i) == J) {
+          constexpr int Q = C::kSteps * C::FN;
+          constexpr int q = KS * C::FN + i;
+          constexpr int L = C::kLoadsPerWave;
+          ld.template issue_part<q * L / Q, (q + 1) * L / Q>(rs, rbuf, wave, lane);
+        }
+      } else {
+        constexpr int FQ = (C::FN >= 4) ? C::FN / 4 : 1;
+        if constexpr (LAST && J == FQ * C::FM - 1) ld.issue(rs, rbuf, wave, lane);
+      }
+    }
+    sched_fence();
+    step_mfmas<C, FAST, REFILL, KS, J + 1>(ld, fc, fn, acc, rstage, rlw, rlx, rs, rbuf, wave, lane);
+  }
+}
+
+// k-steps KS.. of one full stage.  The last k-step first opens the next
+// stage: its loads landed everywhere (wait, barrier), which also means every
+// wave's reads of this stage are done, freeing its buffer for a refill.
+template <class C, bool FAST, bool REFILL, int KS, int KSEND>
+__device__ __forceinline__ void stage_steps(const Loader<C, FAST>& ld, Frags<C> (&f)[2],
+                                            typename C::Acc (&acc)[C::FN][C::FM], const int8_t* cur,
+                                            const int8_t* next, const uint32_t* lw,
+                                            const uint32_t* lx, int rs, int8_t* rbuf, int ahead,
+                                            int wave, int lane) {
+  if constexpr (KS < KSEND) {
+    Frags<C>& fc = f[KS & 1];
+    Frags<C>& fn = f[(KS + 1) & 1];
+    sched_fence();
+    if constexpr (KS + 1 < C::kSteps) {
+      step_mfmas<C, FAST, REFILL, KS, 0>(ld, fc, fn, acc, cur, lw[KS + 1], lx[KS + 1], rs, rbuf,
+                                         wave, lane);
+    } else {
+      wait_next_stage<C, REFILL>(ahead);  // next stage landed (this wave's loads)
+      block_barrier();                    // ... everywhere; this step's fragments too
+      step_mfmas<C, FAST, REFILL, KS, 0>(ld, fc, fn, acc, next, lw[0], lx[0], rs, rbuf, wave,
+                                         lane);
+    }
+    stage_steps<C, FAST, REFILL, KS + 1, KSEND>(ld, f, acc, cur, next, lw, lx, rs, rbuf, ahead, wave,
+                                                lane);
+  }
+}
+
 // One output tile: prologue loads, the K loop, the epilogue.
 template <class C, bool FAST, bool OUT_I32>
 __device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_t m0, int64_t n0,
-                                         int tile_m, int tile_n, int wave, int lane) {
+                                         int wave, int lane) {
   constexpr int S = C::STAGES;
   constexpr int NS = C::kSteps;
   constexpr int SB = C::Op::kStepBytes;
@@ -500,16 +640,21 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_
   const int KST = static_cast<int>((a.K + C::BK - 1) / C::BK);  // stages
 
   Loader<C, FAST> ld(a, n0, m0, wave, lane);
-  // Tiles that share an operand panel run their K loops from different
-  // starting stages (integer accumulation is order-independent, so the result
-  // is the same bit for bit): the first tile to reach a panel stage fetches it,
-  // the others find it in L2 a few stages later instead of all waiting on the
-  // same in-flight misses.  Only whole-stage (FAST) tiles rotate.
-  ld.kst = KST;
-  if constexpr (FAST) ld.koff = KST > 0 ? static_cast<int>(((tile_n + 2 * tile_m) % 8) * 2 % KST) : 0;
+  // All tiles walk K in the same order: the tiles of one XCD that share an
+  // operand panel then ask for the same K slice at about the same time, so
+  // L2 needs to hold only a few stages of each panel.  (Starting tiles at
+  // different K stages instead was measured slower: more L2 misses.)
+  // Every wave issues the same load sequence whatever KST is: the prologue
+  // stages and each stage's refill always go out, stage indices past the end
+  // clamped to the last stage.  Such duplicates land in buffers that are never
+  // read again, and the uniform sequence makes every vmcnt wait below exact.
+  // Spread pipelines prefetch S - 1 stages (stage st refills stage st + S - 1
+  // into the buffer freed just before it); others prefetch S.
+  constexpr int PRO = C::kSpread ? S - 1 : S;
+  if (KST > 0) {
 #pragma unroll
-  for (int s = 0; s < S; ++s)
-    if (s < KST) ld.issue(s, smem + s * C::kStage, wave, lane);
+    for (int s = 0; s < PRO; ++s) ld.issue(min(s, KST - 1), smem + s * C::kStage, wave, lane);
+  }
 
   // fragment addressing: row (MF f + lane % MF), chunk (step SB/16 + lane / MF)
   uint32_t lw[NS], lx[NS];
@@ -530,42 +675,54 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_
     for (int j = 0; j < C::FM; ++j) acc[i][j] = typename C::Acc{};
 
   if (KST > 0) {
-    wait_stages<C>(min(S - 1, KST - 1));  // stage 0 landed
+    wait_stages<C>(PRO - 1);  // stage 0 landed
     block_barrier();
     Frags<C> f[2];
     read_frags<C>(f[0], smem, lw[0], lx[0]);
-    // Full stages; the last (possibly partial) stage is peeled below.
-    // Software pipeline per k-step: make sure this step's fragments have
-    // landed (they were read a whole step earlier), read the next step's
-    // fragments, then issue this step's MFMAs -- the reads get a full MFMA
-    // batch of lead time.  The last step of a stage first opens the next
-    // stage (its loads landed everywhere, then a barrier), and issues the
-    // loads that refill the freed buffer after a quarter of its MFMAs.
-    constexpr int FQ = (C::FN >= 4) ? C::FN / 4 : 1;  // MFMA rows before the load issue
-    for (int st = 0; st < KST - 1; ++st) {
-      const int8_t* cur = smem + (st % S) * C::kStage;
-#pragma unroll
-      for (int ks = 0; ks < NS; ++ks) {
-        Frags<C>& fc = f[ks & 1];
-        Frags<C>& fn = f[(ks + 1) & 1];
-        sched_fence();
-        wait_lds();
-        if (ks + 1 < NS) {
-          read_frags<C>(fn, cur, lw[ks + 1], lx[ks + 1]);
-          sched_fence();
-          mfma_rows<C, 0, C::FN>(fc, acc);
-        } else {
-          wait_stages<C>(min(S - 2, KST - 2 - st));  // stage st+1 landed (this wave)
-          block_barrier();                           // ... everywhere; stage st is free
-          read_frags<C>(fn, smem + ((st + 1) % S) * C::kStage, lw[0], lx[0]);
-          sched_fence();
-          mfma_rows<C, 0, FQ>(fc, acc);
-          sched_fence();
-          if (st + S < KST) ld.issue(st + S, smem + (st % S) * C::kStage, wave, lane);
-          sched_fence();
-          mfma_rows<C, FQ, C::FN>(fc, acc);
-        }
+    // nothing in flight on the LDS / scalar-load counter when the K loop
+    // starts, so the row waits inside it are exact
+    wait_lds();
+    // Full stages; the last (possibly partial) stage is peeled below.  The
+    // stages that refill a buffer run a separately compiled body (no branch
+    // inside the MFMA stream).
+    // Stage st's k-steps run as a head (steps 0 .. NS-2) and a tail (the
+    // last step, which opens stage st + 1).  The loop body is one stage's
+    // tail followed by the next stage's head, so the fragment reads that
+    // cross the loop back edge are always waited for by the tail's barrier
+    // and the row waits inside the body are exact.
+    auto refill_of = [&](int st, int& rs, int8_t*& rbuf) {
+      if constexpr (C::kSpread) {
+        rs = min(st + S - 1, KST - 1);  // into the buffer freed just before
+        rbuf = smem + ((st + S - 1) % S) * C::kStage;
+      } else {
+        rs = min(st + S, KST - 1);      // into this stage's buffer, once the next is open
+        rbuf = smem + (st % S) * C::kStage;
       }
+    };
+    auto head = [&](int st) {
+      int rs;
+      int8_t* rbuf;
+      refill_of(st, rs, rbuf);
+      stage_steps<C, FAST, true, 0, NS - 1>(ld, f, acc, smem + (st % S) * C::kStage,
+                                            smem + ((st + 1) % S) * C::kStage, lw, lx, rs, rbuf,
+                                            S - 2, wave, lane);
+    };
+    auto tail = [&](int st) {
+      int rs;
+      int8_t* rbuf;
+      refill_of(st, rs, rbuf);
+      stage_steps<C, FAST, true, NS - 1, NS>(ld, f, acc, smem + (st % S) * C::kStage,
+                                             smem + ((st + 1) % S) * C::kStage, lw, lx, rs, rbuf,
+                                             S - 2, wave, lane);
+    };
+    const int nfull = KST - 1;  // full stages; the last one is peeled below
+    if (nfull > 0) {
+      head(0);
+      for (int st = 0; st + 1 < nfull; ++st) {
+        tail(st);
+        head(st + 1);
+      }
+      tail(nfull - 1);
     }
     {
       const int st = KST - 1;
@@ -584,6 +741,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_
         mfma_step<C>(f[ks & 1], acc);
       }
     }
+    // the duplicate loads past the last stage must land before the buffers
+    // are reused by a next tile or the workgroup ends
+    wait_vm0();
   }
 #ifndef W8A8_LDS_EPILOGUE
   if constexpr (FAST && !OUT_I32)
@@ -613,9 +773,9 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
                       (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0);
     if (t != static_cast<int>(blockIdx.x)) block_barrier();  // LDS reuse across tiles
     if (fast)
-      run_tile<C, true, OUT_I32>(a, smem, m0, n0, tm, tn, wave, lane);
+      run_tile<C, true, OUT_I32>(a, smem, m0, n0, wave, lane);
     else
-      run_tile<C, false, OUT_I32>(a, smem, m0, n0, tm, tn, wave, lane);
+      run_tile<C, false, OUT_I32>(a, smem, m0, n0, wave, lane);
   }
 }
 
