@@ -6,10 +6,11 @@
 // epilogue folds the two scales and the bias, autotuned per GEMM shape.  The
 // paper's kernel targets Ampere tensor cores; this one is designed for CDNA4:
 //
-//  * MFMA v_mfma_i32_16x16x64_i8.  The weight tile is the MFMA "A" operand and
-//    the activation tile the "B" operand, so a 16x16 result block holds
-//    D[n][m]: each lane owns four consecutive output columns n of one row m,
-//    which the epilogue writes as one 8-byte bf16 store (16 bytes for int32).
+//  * MFMA v_mfma_i32_32x32x32_i8 (v_mfma_i32_16x16x64_i8 for the skinny
+//    tile).  The weight tile is the MFMA "A" operand and the activation tile
+//    the "B" operand, so a result block holds D[n][m]: each lane owns runs of
+//    four consecutive output columns n of one row m, which the epilogue
+//    writes as 8-byte bf16 stores (16 bytes for int32).
 //  * Both operands are K-contiguous ([M,K] and [N,K] row-major), which is what
 //    the MFMA operand layout wants: every lane reads 16 consecutive k of one
 //    row with a single ds_read_b128, no transposes anywhere.
@@ -17,16 +18,18 @@
 //    1 KiB straight into LDS (lane i fills bytes 16i..16i+15 of the block), so
 //    no staging registers and no ds_write instructions.  The XOR swizzle of
 //    the 16-byte chunks inside a row is applied on the global side: a lane
-//    loads the logical chunk that belongs in its fixed LDS slot.
-//  * LDS pipeline of STAGES buffers of BK bytes of K; waits use explicit
-//    vmcnt counts so later stages stay in flight, and raw s_barrier.
-//  * Persistent workgroups walk the tile list; the next tile's first stages
-//    are issued before the current tile's epilogue, so their latency hides
-//    behind the epilogue's arithmetic and stores.
+//    loads the logical chunk that belongs in its fixed LDS slot, and the
+//    fragment reads are free of bank conflicts.
+//  * LDS pipeline of STAGES buffers of BK bytes of K.  One wave per SIMD
+//    (a 256 x 256 tile's 128 x 128 wave tiles fill the accumulator file), so
+//    nothing may stall the wave between MFMAs: fragment reads and refill
+//    loads are woven in one instruction at a time, and every wait uses an
+//    exact vmcnt / lgkmcnt count (see Sched and wait_next_stage).
 //  * Tile order: the dispatcher deals workgroups round-robin to the 8 XCDs,
 //    each with its own L2.  Tile ids are remapped so each XCD receives a
 //    contiguous range, walked in groups of 8 M-tiles, so the workgroups
-//    sharing an L2 also share activation and weight panels.
+//    sharing an L2 also share activation and weight panels, and all walk K
+//    in the same order.
 //  * Epilogue in fp32, no contraction: (s_x[m] * s_w[n]) * float(acc) + bias[n],
 //    rounded once to bf16 (v_cvt_pk_bf16_f32, round to nearest even).  The
 //    int32 accumulators never touch memory unless the int32 debug output is
@@ -292,11 +295,27 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
 }
 
-// (s_x * s_w) * float(acc) [+ bias]: each step one IEEE fp32 operation.
-__device__ __forceinline__ float dequant(int32_t acc, float sx, float sw, float b, bool has_bias) {
+// Two floats to a packed pair of bf16 (round to nearest even), low half first:
+// one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const bf16x2 h = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// The bias term of one output: bias[n] as fp32, or -0.0 without a bias.
+// Adding -0.0 is the identity for every fp32 value (including -0.0), so the
+// epilogue adds unconditionally and a missing bias still adds nothing.
+__device__ __forceinline__ float bias_term(const uint16_t* bias, int64_t n) {
+  return bias ? __uint_as_float(static_cast<uint32_t>(bias[n]) << 16) : -0.0f;
+}
+
+// (s_x * s_w) * float(acc) + b: each step one IEEE fp32 operation.
+__device__ __forceinline__ float dequant(int32_t acc, float sx, float sw, float b) {
   const float f = sx * sw;
   const float v = f * static_cast<float>(acc);
-  return has_bias ? v + b : v;
+  return v + b;
 }
 
 // Lane owns, in each MFMA block, output row m = lane % MF and four runs of
@@ -308,7 +327,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t 
   constexpr int G = C::Op::kGroups;
   const int64_t M = a.M, N = a.N;
   const int lr = lane % MF, lq = lane / MF;
-  const bool hb = a.bias != nullptr;
 #pragma unroll
   for (int fi = 0; fi < C::FN; ++fi) {
     const int64_t nb = n0 + wn * C::TN + fi * MF + lq * 4;
@@ -321,7 +339,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t 
           const int64_t n = nb + g * 8 + e;
           const bool in = !GUARD || n < N;
           sw[g][e] = in ? a.sw[n] : 0.0f;
-          bv[g][e] = (hb && in) ? __uint_as_float(static_cast<uint32_t>(a.bias[n]) << 16) : 0.0f;
+          bv[g][e] = in ? bias_term(a.bias, n) : 0.0f;
         }
     }
 #pragma unroll
@@ -348,19 +366,19 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t 
               if (n + e < N) out[e] = d[4 * g + e];
           }
         } else {
-          uint32_t h[4];
+          float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = bf16_bits(dequant(d[4 * g + e], sx, sw[g][e], bv[g][e], hb));
+          for (int e = 0; e < 4; ++e) v[e] = dequant(d[4 * g + e], sx, sw[g][e], bv[g][e]);
           uint16_t* out = static_cast<uint16_t*>(a.out) + m * N + n;
           if (vec) {
             uint2 pk;
-            pk.x = h[0] | (h[1] << 16);
-            pk.y = h[2] | (h[3] << 16);
+            pk.x = bf16_pair(v[0], v[1]);
+            pk.y = bf16_pair(v[2], v[3]);
             *reinterpret_cast<uint2*>(out) = pk;
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < N) out[e] = static_cast<uint16_t>(h[e]);
+              if (n + e < N) out[e] = static_cast<uint16_t>(bf16_bits(v[e]));
           }
         }
       }
@@ -368,14 +386,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t 
   }
 }
 
-// Interior-tile bf16 epilogue through LDS: each wave dequantizes its
-// accumulators in the MFMA layout and writes 8-byte runs (4 outputs) into a
-// row-major staging tile; then every wave writes whole output rows, 8 bytes
-// per lane, so each store instruction covers BN / 4 lanes' worth of
-// contiguous row bytes (a full 512-byte row for BN = 256).  Staging slots of
-// 8 bytes are XOR-swizzled with the row: the MFMA-layout writes (32 rows at
-// one slot) and the row reads (one row, consecutive slots) are both free of
-// bank conflicts.
 // Interior-tile bf16 epilogue, stored straight from the MFMA layout.  All
 // scales and biases the lane needs are fetched up front with vector loads
 // (four consecutive columns per 16-byte s_w load and 8-byte bias load; both
@@ -388,19 +398,20 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
   constexpr int MF = C::MF;
   constexpr int G = C::Op::kGroups;
   const int lr = lane % MF, lq = lane / MF;
-  const bool hb = a.bias != nullptr;
   float sx[C::FM];
 #pragma unroll
   for (int fj = 0; fj < C::FM; ++fj) sx[fj] = a.sx[m0 + wm * C::TM + fj * MF + lr];
   float4 sw[C::FN][G];
   uint2 bb[C::FN][G];
+  // no bias: every term is -0.0 (bf16 0x8000)
+  const uint2 nobias = make_uint2(0x80008000u, 0x80008000u);
 #pragma unroll
   for (int fi = 0; fi < C::FN; ++fi)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
       sw[fi][g] = *reinterpret_cast<const float4*>(a.sw + n);
-      bb[fi][g] = hb ? *reinterpret_cast<const uint2*>(a.bias + n) : make_uint2(0u, 0u);
+      bb[fi][g] = a.bias ? *reinterpret_cast<const uint2*>(a.bias + n) : nobias;
     }
   uint16_t* y = static_cast<uint16_t*>(a.out);
 #pragma unroll
@@ -416,78 +427,15 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
         const float swv[4] = {sw[fi][g].x, sw[fi][g].y, sw[fi][g].z, sw[fi][g].w};
         const float bv[4] = {__uint_as_float(bb[fi][g].x << 16), __uint_as_float(bb[fi][g].x & 0xFFFF0000u),
                              __uint_as_float(bb[fi][g].y << 16), __uint_as_float(bb[fi][g].y & 0xFFFF0000u)};
-        uint32_t h[4];
+        float v[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = bf16_bits(dequant(d[4 * g + e], sx[fj], swv[e], bv[e], hb));
+        for (int e = 0; e < 4; ++e) v[e] = dequant(d[4 * g + e], sx[fj], swv[e], bv[e]);
         uint2 pk;
-        pk.x = h[0] | (h[1] << 16);
-        pk.y = h[2] | (h[3] << 16);
+        pk.x = bf16_pair(v[0], v[1]);
+        pk.y = bf16_pair(v[2], v[3]);
         *reinterpret_cast<uint2*>(y + m * a.N + n) = pk;
       }
     }
-  }
-}
-
-template <class C>
-__device__ __forceinline__ int stage_slot(int row, int slot) {
-  constexpr int SLOTS = C::BN / 4;  // 8-byte slots per staged row
-  constexpr int MASK = SLOTS >= 32 ? 31 : SLOTS - 1;
-  return slot ^ (row & MASK);
-}
-
-template <class C>
-__device__ __forceinline__ void epilogue_lds(const GemmArgs& a, int8_t* smem, int64_t m0, int64_t n0,
-                                             int wn, int wm, int wave, int lane,
-                                             const typename C::Acc (&acc)[C::FN][C::FM]) {
-  constexpr int MF = C::MF;
-  constexpr int G = C::Op::kGroups;
-  constexpr int SLOTS = C::BN / 4;
-  static_assert(C::BM * C::BN * 2 <= C::STAGES * C::kStage, "staging tile fits the LDS stages");
-  const int lr = lane % MF, lq = lane / MF;
-  const bool hb = a.bias != nullptr;
-  block_barrier();  // all waves are done reading the operand stages
-#pragma unroll
-  for (int fi = 0; fi < C::FN; ++fi) {
-    const int nl = wn * C::TN + fi * MF + lq * 4;  // local column of run g = 0
-    float sw[G][4], bv[G][4];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t n = n0 + nl + g * 8 + e;
-        sw[g][e] = a.sw[n];
-        bv[g][e] = hb ? __uint_as_float(static_cast<uint32_t>(a.bias[n]) << 16) : 0.0f;
-      }
-#pragma unroll
-    for (int fj = 0; fj < C::FM; ++fj) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int ml = wm * C::TM + fj * MF + lr;
-      const float sx = a.sx[m0 + ml];
-      const typename C::Acc d = acc[fi][fj];
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        uint32_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) h[e] = bf16_bits(dequant(d[4 * g + e], sx, sw[g][e], bv[g][e], hb));
-        uint2 pk;
-        pk.x = h[0] | (h[1] << 16);
-        pk.y = h[2] | (h[3] << 16);
-        const int slot = (nl + g * 8) / 4;
-        *reinterpret_cast<uint2*>(smem + ml * (C::BN * 2) + stage_slot<C>(ml, slot) * 8) = pk;
-      }
-    }
-  }
-  block_barrier();
-  // rows out: wave instruction i covers rows (wave + i * kWaves) * RPW .. + RPW
-  constexpr int RPW = 64 / SLOTS > 0 ? 64 / SLOTS : 1;  // rows per wave instruction
-  static_assert(SLOTS <= 64 && 64 % SLOTS == 0, "staged row is a whole number of lanes");
-  const int rsub = lane / SLOTS, slot = lane % SLOTS;
-  uint16_t* y = static_cast<uint16_t*>(a.out);
-#pragma unroll 4
-  for (int r0 = wave * RPW; r0 < C::BM; r0 += C::kWaves * RPW) {
-    const int row = r0 + rsub;
-    const uint2 v = *reinterpret_cast<const uint2*>(smem + row * (C::BN * 2) + stage_slot<C>(row, slot) * 8);
-    *reinterpret_cast<uint2*>(y + (m0 + row) * a.N + n0 + slot * 4) = v;
   }
 }
 
@@ -745,13 +693,8 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_
     // are reused by a next tile or the workgroup ends
     wait_vm0();
   }
-#ifndef W8A8_LDS_EPILOGUE
   if constexpr (FAST && !OUT_I32)
     epilogue_fast<C>(a, m0, n0, wn, wm, lane, acc);
-#else
-  if constexpr (FAST && !OUT_I32)
-    epilogue_lds<C>(a, smem, m0, n0, wn, wm, wave, lane, acc);
-#endif
   else
     epilogue<C, OUT_I32, !FAST>(a, m0, n0, wn, wm, lane, acc);
 }
@@ -795,6 +738,7 @@ using C3 = Tile<128, 256, 2, 2, 64, 4, 32>;   // wave tile 64(m) x 128(n)
 using C4 = Tile<128, 128, 2, 2, 64, 4, 32>;   // wave tile 64 x 64
 using C5 = Tile<64, 64, 2, 2, 128, 2, 32>;    // wave tile 32 x 32
 using C6 = Tile<16, 64, 1, 4, 128, 2, 16>;    // wave tile 16 x 16 (skinny M)
+using C7 = Tile<256, 192, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 96(n)
 
 const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 1.00f},
@@ -804,9 +748,10 @@ const ConfigInfo kConfigs[] = {
     {"bm128_bn128_bk64_s4_mf32", 128, 128, 256, 2, 0.70f},
     {"bm64_bn64_bk128_s2_mf32", 64, 64, 256, 4, 0.40f},
     {"bm16_bn64_bk128_s2_mf16", 16, 64, 256, 4, 0.15f},
+    {"bm256_bn192_bk64_s4_mf32", 256, 192, 256, 1, 0.92f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-constexpr int kSkinny = kNumConfigs - 1;
+constexpr int kSkinny = 6;
 constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
 template <class C, bool I32>
@@ -845,7 +790,8 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   if (M <= 16) return kSkinny;
   int best = 0;
   double best_cost = 1e300;
-  for (int c = 0; c < kNumConfigs - 1; ++c) {
+  for (int c = 0; c < kNumConfigs; ++c) {
+    if (c == kSkinny) continue;
     const ConfigInfo& ci = kConfigs[c];
     const double tiles = static_cast<double>((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
     const double slots = static_cast<double>(kNumCU) * ci.wg_per_cu;
@@ -870,6 +816,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 4: return launch_cfg_out<C4>(a, out_int32, stream);
     case 5: return launch_cfg_out<C5>(a, out_int32, stream);
     case 6: return launch_cfg_out<C6>(a, out_int32, stream);
+    case 7: return launch_cfg_out<C7>(a, out_int32, stream);
     default: return hipErrorInvalidValue;
   }
 }
