@@ -414,26 +414,48 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
       bb[fi][g] = a.bias ? *reinterpret_cast<const uint2*>(a.bias + n) : nobias;
     }
   uint16_t* y = static_cast<uint16_t*>(a.out);
+  // row blocks outermost: the 16 stores of one row block complete its
+  // output rows' 256-byte runs back to back, so L2 merges whole lines
+  // before it writes them back (interleaving row blocks left half-written
+  // lines to be written back twice)
 #pragma unroll
-  for (int fi = 0; fi < C::FN; ++fi) {
+  for (int fj = 0; fj < C::FM; ++fj) {
 #pragma unroll
-    for (int fj = 0; fj < C::FM; ++fj) {
+    for (int fi = 0; fi < C::FN; ++fi) {
       __builtin_amdgcn_sched_barrier(0);
       const int64_t m = m0 + wm * C::TM + fj * MF + lr;
       const typename C::Acc d = acc[fi][fj];
+      uint2 pk[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
         const float swv[4] = {sw[fi][g].x, sw[fi][g].y, sw[fi][g].z, sw[fi][g].w};
         const float bv[4] = {__uint_as_float(bb[fi][g].x << 16), __uint_as_float(bb[fi][g].x & 0xFFFF0000u),
                              __uint_as_float(bb[fi][g].y << 16), __uint_as_float(bb[fi][g].y & 0xFFFF0000u)};
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = dequant(d[4 * g + e], sx[fj], swv[e], bv[e]);
-        uint2 pk;
-        pk.x = bf16_pair(v[0], v[1]);
-        pk.y = bf16_pair(v[2], v[3]);
-        *reinterpret_cast<uint2*>(y + m * a.N + n) = pk;
+        pk[g].x = bf16_pair(v[0], v[1]);
+        pk[g].y = bf16_pair(v[2], v[3]);
+      }
+      const int64_t nb = n0 + wn * C::TN + fi * MF;
+      if constexpr (G % 2 == 0) {
+        // Lanes l and l + 32 hold the two 4-column halves of each 8-column
+        // group of row m.  Swap so that lane l holds group 2p whole and lane
+        // l + 32 group 2p + 1 (v_permlane32_swap exchanges the upper half of
+        // the first operand with the lower half of the second): one 16-byte
+        // store per lane and pair of groups.
+#pragma unroll
+        for (int p = 0; p < G / 2; ++p) {
+          const auto sx2 = __builtin_amdgcn_permlane32_swap(pk[2 * p].x, pk[2 * p + 1].x, false, false);
+          const auto sy2 = __builtin_amdgcn_permlane32_swap(pk[2 * p].y, pk[2 * p + 1].y, false, false);
+          const uint4 o = make_uint4(sx2[0], sy2[0], sx2[1], sy2[1]);
+          const int64_t n = nb + (2 * p + lq) * 8;
+          *reinterpret_cast<uint4*>(y + m * a.N + n) = o;
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          *reinterpret_cast<uint2*>(y + m * a.N + nb + lq * 4 + g * 8) = pk[g];
       }
     }
   }
@@ -711,7 +733,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
     const int64_t m0 = static_cast<int64_t>(tm) * C::BM;
     const int64_t n0 = static_cast<int64_t>(tn) * C::BN;
     // interior tile, whole stages in K, and vector-aligned scales / bias
-    const bool fast = (m0 + C::BM <= a.M) && (n0 + C::BN <= a.N) && (a.N % 4 == 0) &&
+    const bool fast = (m0 + C::BM <= a.M) && (n0 + C::BN <= a.N) && (a.N % 8 == 0) &&
                       (a.K % C::BK == 0) && (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
                       (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0);
     if (t != static_cast<int>(blockIdx.x)) block_barrier();  // LDS reuse across tiles
