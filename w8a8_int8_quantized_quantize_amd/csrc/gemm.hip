@@ -49,6 +49,7 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) int8_t global_i8;
 
 constexpr int kGroupM = 8;  // M-tiles per group in the grouped tile order
 
@@ -190,6 +191,15 @@ __device__ __forceinline__ const int8_t* sgpr_ptr(const int8_t* p) {
   return reinterpret_cast<const int8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// The same as a global-address-space pointer (its loads can then take the
+// scalar-base + 32-bit vector-offset form).
+__device__ __forceinline__ const global_i8* sgpr_gptr(const int8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const global_i8*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Stage loads.  Block j of a stage covers rows [j R, (j+1) R) of the
 // concatenated [BN weight rows | BM activation rows] tile, R = 1024 / BK;
 // lane i fills row j R + i / SLOTS at physical slot i % SLOTS, i.e. it loads
@@ -235,7 +245,12 @@ struct Loader {
       const int64_t g0 = (is_w ? n0 : m0) + row0;
       lds_void* d = (lds_void*)(dst + j * 1024);
       if constexpr (FAST) {
-        const int8_t* g = sgpr_ptr(op + g0 * K + k0) + lane_off;
+        // opaque lane offset: keeps the address a scalar base plus a 32-bit
+        // vector offset (the scalar-base form of the load) instead of letting
+        // the compiler hoist one 64-bit vector address per load slot
+        uint32_t off = lane_off;
+        asm volatile("" : "+v"(off));
+        const global_i8* g = sgpr_gptr(op + g0 * K + k0) + off;
         __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
       } else {
         const int lr = lane / C::kSlots, p = lane % C::kSlots;
@@ -398,9 +413,15 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
   constexpr int MF = C::MF;
   constexpr int G = C::Op::kGroups;
   const int lr = lane % MF, lq = lane / MF;
+  // opaque bases: the scale / bias loads below must not be hoisted above the
+  // K loop, where their ~100 registers would crowd out the loop's
+  const float* sxp = a.sx;
+  const float* swp = a.sw;
+  const uint16_t* bp = a.bias;
+  asm volatile("" : "+s"(sxp), "+s"(swp), "+s"(bp));
   float sx[C::FM];
 #pragma unroll
-  for (int fj = 0; fj < C::FM; ++fj) sx[fj] = a.sx[m0 + wm * C::TM + fj * MF + lr];
+  for (int fj = 0; fj < C::FM; ++fj) sx[fj] = sxp[m0 + wm * C::TM + fj * MF + lr];
   float4 sw[C::FN][G];
   uint2 bb[C::FN][G];
   // no bias: every term is -0.0 (bf16 0x8000)
@@ -410,8 +431,8 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
-      sw[fi][g] = *reinterpret_cast<const float4*>(a.sw + n);
-      bb[fi][g] = a.bias ? *reinterpret_cast<const uint2*>(a.bias + n) : nobias;
+      sw[fi][g] = *reinterpret_cast<const float4*>(swp + n);
+      bb[fi][g] = bp ? *reinterpret_cast<const uint2*>(bp + n) : nobias;
     }
   uint16_t* y = static_cast<uint16_t*>(a.out);
   // row blocks outermost: the 16 stores of one row block complete its
@@ -599,32 +620,47 @@ __device__ __forceinline__ void stage_steps(const Loader<C, FAST>& ld, Frags<C> 
   }
 }
 
-// One output tile: prologue loads, the K loop, the epilogue.
-template <class C, bool FAST, bool OUT_I32>
-__device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_t m0, int64_t n0,
-                                         int wave, int lane) {
+// Stages the prologue of a tile loads before its K loop.  Every wave issues
+// the same load sequence whatever KST is: the prologue stages and each
+// stage's refill always go out, stage indices past the end clamped to the
+// last stage.  Such duplicates land in buffers that are never read again,
+// and the uniform sequence makes every vmcnt wait exact.  Spread pipelines
+// prefetch S - 1 stages (stage st refills stage st + S - 1 into the buffer
+// freed just before it); others prefetch S.
+template <class C>
+constexpr int kPrologue = C::kSpread ? C::STAGES - 1 : C::STAGES;
+
+// A tile's prologue loads (all LDS buffers must be free).
+template <class C, bool FAST>
+__device__ __forceinline__ void tile_prologue(const GemmArgs& a, int8_t* smem, int64_t m0,
+                                              int64_t n0, int wave, int lane) {
+  const int KST = static_cast<int>((a.K + C::BK - 1) / C::BK);
+  if (KST > 0) {
+    Loader<C, FAST> ld(a, n0, m0, wave, lane);
+#pragma unroll
+    for (int s = 0; s < kPrologue<C>; ++s)
+      ld.issue(min(s, KST - 1), smem + s * C::kStage, wave, lane);
+  }
+}
+
+// A tile's K loop, from its prologue's loads to the accumulators.  All tiles
+// walk K in the same order: the tiles of one XCD that share an operand panel
+// then ask for the same K slice at about the same time, so L2 needs to hold
+// only a few stages of each panel.  (Starting tiles at different K stages
+// instead was measured slower: more L2 misses.)  Loads and stores return in
+// issue order, so the first wait below also covers stores the previous
+// tile's epilogue issued after this tile's prologue loads.
+template <class C, bool FAST>
+__device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, int64_t m0,
+                                              int64_t n0, int wave, int lane,
+                                              typename C::Acc (&acc)[C::FN][C::FM]) {
   constexpr int S = C::STAGES;
   constexpr int NS = C::kSteps;
   constexpr int SB = C::Op::kStepBytes;
+  constexpr int PRO = kPrologue<C>;
   const int wn = wave % C::WN, wm = wave / C::WN;
   const int KST = static_cast<int>((a.K + C::BK - 1) / C::BK);  // stages
-
   Loader<C, FAST> ld(a, n0, m0, wave, lane);
-  // All tiles walk K in the same order: the tiles of one XCD that share an
-  // operand panel then ask for the same K slice at about the same time, so
-  // L2 needs to hold only a few stages of each panel.  (Starting tiles at
-  // different K stages instead was measured slower: more L2 misses.)
-  // Every wave issues the same load sequence whatever KST is: the prologue
-  // stages and each stage's refill always go out, stage indices past the end
-  // clamped to the last stage.  Such duplicates land in buffers that are never
-  // read again, and the uniform sequence makes every vmcnt wait below exact.
-  // Spread pipelines prefetch S - 1 stages (stage st refills stage st + S - 1
-  // into the buffer freed just before it); others prefetch S.
-  constexpr int PRO = C::kSpread ? S - 1 : S;
-  if (KST > 0) {
-#pragma unroll
-    for (int s = 0; s < PRO; ++s) ld.issue(min(s, KST - 1), smem + s * C::kStage, wave, lane);
-  }
 
   // fragment addressing: row (MF f + lane % MF), chunk (step SB/16 + lane / MF)
   uint32_t lw[NS], lx[NS];
@@ -638,7 +674,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_
     }
   }
 
-  typename C::Acc acc[C::FN][C::FM];
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -715,32 +750,86 @@ __device__ __forceinline__ void run_tile(const GemmArgs& a, int8_t* smem, int64_
     // are reused by a next tile or the workgroup ends
     wait_vm0();
   }
+}
+
+template <class C, bool FAST, bool OUT_I32>
+__device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int64_t m0, int64_t n0, int wave,
+                                              int lane, const typename C::Acc (&acc)[C::FN][C::FM]) {
+  const int wn = wave % C::WN, wm = wave / C::WN;
   if constexpr (FAST && !OUT_I32)
     epilogue_fast<C>(a, m0, n0, wn, wm, lane, acc);
   else
     epilogue<C, OUT_I32, !FAST>(a, m0, n0, wn, wm, lane, acc);
 }
 
+template <class C>
+__device__ __forceinline__ bool tile_is_fast(const GemmArgs& a, int64_t m0, int64_t n0) {
+  // interior tile, whole stages in K, 16-byte output rows, and vector-aligned
+  // scales / bias
+  return (m0 + C::BM <= a.M) && (n0 + C::BN <= a.N) && (a.N % 8 == 0) && (a.K % C::BK == 0) &&
+         (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
+         (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0);
+}
+
+// Persistent workgroups: workgroup b takes tiles b, b + G, b + 2G, ... (G =
+// grid size, a multiple of 8 when there are more tiles than workgroups, so
+// each workgroup stays on one XCD's tile range).  The next tile's prologue
+// loads go out before the current tile's epilogue, so their latency hides
+// behind its arithmetic and stores.
 template <class C, bool OUT_I32>
 __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, int MT, int NT) {
   __shared__ __attribute__((aligned(1024))) int8_t smem[C::STAGES * C::kStage];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  // normally one tile per workgroup; grids are capped for huge problems
-  for (int t = blockIdx.x; t < T; t += gridDim.x) {
-    int tm, tn;
-    tile_coords(t, T, MT, NT, tm, tn);
-    const int64_t m0 = static_cast<int64_t>(tm) * C::BM;
-    const int64_t n0 = static_cast<int64_t>(tn) * C::BN;
-    // interior tile, whole stages in K, and vector-aligned scales / bias
-    const bool fast = (m0 + C::BM <= a.M) && (n0 + C::BN <= a.N) && (a.N % 8 == 0) &&
-                      (a.K % C::BK == 0) && (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
-                      (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0);
-    if (t != static_cast<int>(blockIdx.x)) block_barrier();  // LDS reuse across tiles
+  int t = blockIdx.x;
+  if (t >= T) return;
+  int tm, tn;
+  tile_coords(t, T, MT, NT, tm, tn);
+  int64_t m0 = static_cast<int64_t>(tm) * C::BM, n0 = static_cast<int64_t>(tn) * C::BN;
+  bool fast = tile_is_fast<C>(a, m0, n0);
+  if (fast)
+    tile_prologue<C, true>(a, smem, m0, n0, wave, lane);
+  else
+    tile_prologue<C, false>(a, smem, m0, n0, wave, lane);
+  typename C::Acc acc[C::FN][C::FM];
+  for (;;) {
+    // opaque per tile: lane- and wave-derived offsets are recomputed for
+    // each tile instead of being hoisted out of the tile loop, where their
+    // registers would be held through every K loop
+    int ln = lane, wv = wave;
+    asm volatile("" : "+v"(ln), "+s"(wv));
     if (fast)
-      run_tile<C, true, OUT_I32>(a, smem, m0, n0, wave, lane);
+      tile_mainloop<C, true>(a, smem, m0, n0, wv, ln, acc);
     else
-      run_tile<C, false, OUT_I32>(a, smem, m0, n0, wave, lane);
+      tile_mainloop<C, false>(a, smem, m0, n0, wv, ln, acc);
+    const int tnext = t + static_cast<int>(gridDim.x);
+    const bool more = tnext < T;
+    int64_t m1 = 0, n1 = 0;
+    bool fast1 = false;
+    if (more) {
+      tile_coords(tnext, T, MT, NT, tm, tn);
+      m1 = static_cast<int64_t>(tm) * C::BM;
+      n1 = static_cast<int64_t>(tn) * C::BN;
+      fast1 = tile_is_fast<C>(a, m1, n1);
+      block_barrier();  // every wave is done reading this tile's LDS buffers
+      int ln1 = lane, wv1 = wave;
+      asm volatile("" : "+v"(ln1), "+s"(wv1));
+      if (fast1)
+        tile_prologue<C, true>(a, smem, m1, n1, wv1, ln1);
+      else
+        tile_prologue<C, false>(a, smem, m1, n1, wv1, ln1);
+    }
+    int ln2 = lane, wv2 = wave;
+    asm volatile("" : "+v"(ln2), "+s"(wv2));
+    if (fast)
+      tile_epilogue<C, true, OUT_I32>(a, m0, n0, wv2, ln2, acc);
+    else
+      tile_epilogue<C, false, OUT_I32>(a, m0, n0, wv2, ln2, acc);
+    if (!more) break;
+    t = tnext;
+    m0 = m1;
+    n0 = n1;
+    fast = fast1;
   }
 }
 
@@ -782,9 +871,17 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t NT = (a.N + C::BN - 1) / C::BN;
   const int64_t T = MT * NT;
   if (T > INT32_MAX) return hipErrorInvalidValue;
-  // grid x threads must stay below 2^32 work-items; a multiple of the 8 XCDs
-  const int64_t cap = ((0xFFFFFFFFll / C::kThreads) / 8) * 8;
-  const int grid = static_cast<int>(T < cap ? T : cap);
+  // Persistent grid: as many workgroups as fit on the device at once (a
+  // multiple of the 8 XCDs), or one per tile if there are fewer tiles.
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_kernel<C, I32>, C::kThreads, 0);
+  if (e != hipSuccess) return e;
+  int64_t resident = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : 1);
+  resident = resident >= 8 ? (resident / 8) * 8 : resident;
+  const int grid = static_cast<int>(T < resident ? T : resident);
   gemm_kernel<C, I32><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
       a, static_cast<int>(T), static_cast<int>(MT), static_cast<int>(NT));
   return hipGetLastError();
