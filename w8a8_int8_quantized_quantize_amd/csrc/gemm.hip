@@ -122,6 +122,12 @@ struct Tile {
   static_assert(STAGES >= 2 && STAGES * kStage <= 160 * 1024, "LDS budget");
 };
 
+// Store instructions one wave of the interior-tile bf16 epilogue issues
+// (one per pair of 4-column groups when the groups pair up).
+template <class C>
+constexpr int kFastStores =
+    C::Op::kGroups % 2 == 0 ? C::FM * C::FN * C::Op::kGroups / 2 : C::FM * C::FN * C::Op::kGroups;
+
 // Map a linear tile index to (tile_m, tile_n): XCD-contiguous ranges, then
 // grouped order inside a range.
 __device__ __forceinline__ void tile_coords(int t, int T, int MT, int NT, int& tm, int& tn) {
@@ -230,9 +236,19 @@ struct Loader {
     issue_part<0, C::kLoadsPerWave>(s, dst, wave, lane);
   }
 
-  // This wave's loads [J0, J1) of stage s.
+  // This wave's loads [J0, J1) of stage s of its own tile.
   template <int J0, int J1>
   __device__ __forceinline__ void issue_part(int s, int8_t* dst, int wave, int lane) const {
+    issue_part_at<J0, J1>(n0, m0, s, dst, wave, lane);
+  }
+
+  // This wave's loads [J0, J1) of stage s of the tile at (n0t, m0t).  The
+  // fast path may load for another interior tile than the loader's own (the
+  // next tile of a persistent workgroup); the guarded path is only ever used
+  // with its own tile.
+  template <int J0, int J1>
+  __device__ __forceinline__ void issue_part_at(int64_t n0t, int64_t m0t, int s, int8_t* dst,
+                                                int wave, int lane) const {
     if constexpr (J0 >= J1) return;
     const int64_t k0 = static_cast<int64_t>(s) * C::BK;
 #pragma unroll
@@ -242,7 +258,7 @@ struct Loader {
       const bool is_w = jj < kWBlocksPerWave;  // compile-time after unrolling
       const int row0 = is_w ? j * R : j * R - C::BN;
       const int8_t* op = is_w ? qw : qx;
-      const int64_t g0 = (is_w ? n0 : m0) + row0;
+      const int64_t g0 = (is_w ? n0t : m0t) + row0;
       lds_void* d = (lds_void*)(dst + j * 1024);
       if constexpr (FAST) {
         // opaque lane offset: keeps the address a scalar base plus a 32-bit
@@ -493,14 +509,16 @@ __device__ __forceinline__ void zero_tail(Frags<C>& fr, int64_t kstep0, int64_t 
 // Wait for the next stage's loads (this wave's) at the end of a stage.
 // `ahead` whole later stages may stay in flight; with spread refills the
 // last of them is only partly issued at this point.
-template <class C, bool REFILL>
+// XST: the previous tile's epilogue stores (kFastStores of them) were issued
+// after stage st + 1's loads and may stay in flight too.
+template <class C, bool REFILL, bool XST = false>
 __device__ __forceinline__ void wait_next_stage(int ahead) {
   if constexpr (C::kSpread && REFILL) {
     // after stage st + 1's loads: stages st + 2 .. st + S - 2 whole, and the
     // part of stage st + S - 1 issued in this stage's earlier k-steps
     constexpr int L = C::kLoadsPerWave;
     constexpr int P = L * (C::kSteps - 1) / C::kSteps;
-    wait_vm<(C::STAGES - 3) * L + P>();
+    wait_vm<(C::STAGES - 3) * L + P + (XST ? kFastStores<C> : 0)>();
   } else {
     wait_stages<C>(ahead);
   }
@@ -557,13 +575,21 @@ __device__ __forceinline__ void wait_lgkm() {
   __builtin_amdgcn_s_waitcnt(waitcnt_imm<63, N>());
 }
 
+// Where one stage's refill loads go: stage `s` of the tile at (n0, m0)
+// into LDS buffer `buf`.
+struct Refill {
+  int64_t n0, m0;
+  int s;
+  int8_t* buf;
+};
+
 // MFMAs J.. of k-step KS with the reads of the following k-step (into fn,
-// from stage `rstage`) and the refill slices woven in.
-template <class C, bool FAST, bool REFILL, int KS, int J>
+// from stage `rstage`; none if !READ) and the refill slices woven in.
+template <class C, bool FAST, bool READ, bool EXT, int KS, int J>
 __device__ __forceinline__ void step_mfmas(const Loader<C, FAST>& ld, const Frags<C>& fc,
                                            Frags<C>& fn, typename C::Acc (&acc)[C::FN][C::FM],
-                                           const int8_t* rstage, uint32_t rlw, uint32_t rlx, int rs,
-                                           int8_t* rbuf, int wave, int lane) {
+                                           const int8_t* rstage, uint32_t rlw, uint32_t rlx,
+                                           const Refill& rf, int wave, int lane) {
   using Sc = Sched<C>;
   constexpr bool LAST = KS + 1 == C::kSteps;
   if constexpr (J < Sc::NM) {
@@ -572,65 +598,77 @@ __device__ __forceinline__ void step_mfmas(const Loader<C, FAST>& ld, const Frag
     sched_fence();
     acc[i][jj] = C::Op::run(fc.w[i], fc.x[jj], acc[i][jj]);
     sched_fence();
+    if constexpr (READ) {
 #pragma unroll
-    for (int r = 0; r < Sc::R; ++r)
-      if (Sc::read_after(LAST, r) == J) read_frag<C>(fn, r, rstage, rlw, rlx);
-    if constexpr (REFILL) {
-      if constexpr (C::kSpread) {
-        if constexpr (Sc::dma_after(i) == J) {
-          constexpr int Q = C::kSteps * C::FN;
-          constexpr int q = KS * C::FN + i;
-          constexpr int L = C::kLoadsPerWave;
-          ld.template issue_part<q * L / Q, (q + 1) * L / Q>(rs, rbuf, wave, lane);
-        }
-      } else {
-        constexpr int FQ = (C::FN >= 4) ? C::FN / 4 : 1;
-        if constexpr (LAST && J == FQ * C::FM - 1) ld.issue(rs, rbuf, wave, lane);
+      for (int r = 0; r < Sc::R; ++r)
+        if (Sc::read_after(LAST, r) == J) read_frag<C>(fn, r, rstage, rlw, rlx);
+    }
+    if constexpr (C::kSpread) {
+      if constexpr (Sc::dma_after(i) == J) {
+        constexpr int Q = C::kSteps * C::FN;
+        constexpr int q = KS * C::FN + i;
+        constexpr int L = C::kLoadsPerWave;
+        if constexpr (EXT)
+          ld.template issue_part_at<q * L / Q, (q + 1) * L / Q>(rf.n0, rf.m0, rf.s, rf.buf, wave,
+                                                                 lane);
+        else
+          ld.template issue_part<q * L / Q, (q + 1) * L / Q>(rf.s, rf.buf, wave, lane);
       }
+    } else {
+      constexpr int FQ = (C::FN >= 4) ? C::FN / 4 : 1;
+      if constexpr (LAST && J == FQ * C::FM - 1)
+        ld.template issue_part<0, C::kLoadsPerWave>(rf.s, rf.buf, wave, lane);
     }
     sched_fence();
-    step_mfmas<C, FAST, REFILL, KS, J + 1>(ld, fc, fn, acc, rstage, rlw, rlx, rs, rbuf, wave, lane);
+    step_mfmas<C, FAST, READ, EXT, KS, J + 1>(ld, fc, fn, acc, rstage, rlw, rlx, rf, wave, lane);
   }
 }
 
-// k-steps KS.. of one full stage.  The last k-step first opens the next
-// stage: its loads landed everywhere (wait, barrier), which also means every
-// wave's reads of this stage are done, freeing its buffer for a refill.
-template <class C, bool FAST, bool REFILL, int KS, int KSEND>
+// k-steps KS .. KSEND-1 of one full stage.  With OPEN, the last k-step first
+// opens the next stage: its loads landed everywhere (wait, barrier), which
+// also means every wave's reads of this stage are done, freeing its buffer
+// for a refill; and it reads the next stage's first fragments.  Without
+// OPEN (a tile's last stage) it only waits for its own fragments.
+template <class C, bool FAST, bool OPEN, bool EXT, int KS, int KSEND, bool XST = false>
 __device__ __forceinline__ void stage_steps(const Loader<C, FAST>& ld, Frags<C> (&f)[2],
                                             typename C::Acc (&acc)[C::FN][C::FM], const int8_t* cur,
                                             const int8_t* next, const uint32_t* lw,
-                                            const uint32_t* lx, int rs, int8_t* rbuf, int ahead,
+                                            const uint32_t* lx, const Refill& rf, int ahead,
                                             int wave, int lane) {
   if constexpr (KS < KSEND) {
     Frags<C>& fc = f[KS & 1];
     Frags<C>& fn = f[(KS + 1) & 1];
     sched_fence();
     if constexpr (KS + 1 < C::kSteps) {
-      step_mfmas<C, FAST, REFILL, KS, 0>(ld, fc, fn, acc, cur, lw[KS + 1], lx[KS + 1], rs, rbuf,
-                                         wave, lane);
+      step_mfmas<C, FAST, true, EXT, KS, 0>(ld, fc, fn, acc, cur, lw[KS + 1], lx[KS + 1], rf, wave,
+                                            lane);
+    } else if constexpr (OPEN) {
+      wait_next_stage<C, true, XST>(ahead);  // next stage landed (this wave's loads)
+      block_barrier();                  // ... everywhere; this step's fragments too
+      step_mfmas<C, FAST, true, EXT, KS, 0>(ld, fc, fn, acc, next, lw[0], lx[0], rf, wave, lane);
     } else {
-      wait_next_stage<C, REFILL>(ahead);  // next stage landed (this wave's loads)
-      block_barrier();                    // ... everywhere; this step's fragments too
-      step_mfmas<C, FAST, REFILL, KS, 0>(ld, fc, fn, acc, next, lw[0], lx[0], rs, rbuf, wave,
-                                         lane);
+      wait_lds();
+      step_mfmas<C, FAST, false, EXT, KS, 0>(ld, fc, fn, acc, next, lw[0], lx[0], rf, wave, lane);
     }
-    stage_steps<C, FAST, REFILL, KS + 1, KSEND>(ld, f, acc, cur, next, lw, lx, rs, rbuf, ahead, wave,
-                                                lane);
+    stage_steps<C, FAST, OPEN, EXT, KS + 1, KSEND, XST>(ld, f, acc, cur, next, lw, lx, rf, ahead,
+                                                        wave, lane);
   }
 }
 
 // Stages the prologue of a tile loads before its K loop.  Every wave issues
 // the same load sequence whatever KST is: the prologue stages and each
-// stage's refill always go out, stage indices past the end clamped to the
-// last stage.  Such duplicates land in buffers that are never read again,
-// and the uniform sequence makes every vmcnt wait exact.  Spread pipelines
-// prefetch S - 1 stages (stage st refills stage st + S - 1 into the buffer
-// freed just before it); others prefetch S.
+// stage's refill always go out.  Spread pipelines prefetch S - 1 stages
+// (stage st refills stage st + S - 1 into the buffer freed just before it);
+// others prefetch S.  Refills past a tile's last stage load the first stages
+// of the workgroup's next tile when both are interior tiles (so that tile
+// needs no prologue); otherwise they repeat the last stage, into buffers
+// that are never read again.  The uniform sequence makes every vmcnt wait
+// exact.
 template <class C>
 constexpr int kPrologue = C::kSpread ? C::STAGES - 1 : C::STAGES;
 
-// A tile's prologue loads (all LDS buffers must be free).
+// A tile's prologue loads (all LDS buffers must be free), stage s into
+// buffer s.
 template <class C, bool FAST>
 __device__ __forceinline__ void tile_prologue(const GemmArgs& a, int8_t* smem, int64_t m0,
                                               int64_t n0, int wave, int lane) {
@@ -643,16 +681,20 @@ __device__ __forceinline__ void tile_prologue(const GemmArgs& a, int8_t* smem, i
   }
 }
 
-// A tile's K loop, from its prologue's loads to the accumulators.  All tiles
-// walk K in the same order: the tiles of one XCD that share an operand panel
-// then ask for the same K slice at about the same time, so L2 needs to hold
-// only a few stages of each panel.  (Starting tiles at different K stages
-// instead was measured slower: more L2 misses.)  Loads and stores return in
-// issue order, so the first wait below also covers stores the previous
-// tile's epilogue issued after this tile's prologue loads.
+// A tile's K loop, from its first stages' loads to the accumulators.  The
+// tile's stage st lives in LDS buffer (ph + st) % S.  With `chain` (spread
+// pipelines, this and the next tile both interior) the last refills load the
+// next tile at (n1, m1), whose phase is then (ph + KST) % S.  All tiles walk
+// K in the same order: the tiles of one XCD that share an operand panel then
+// ask for the same K slice at about the same time, so L2 needs to hold only
+// a few stages of each panel.  (Starting tiles at different K stages instead
+// was measured slower: more L2 misses.)  Loads and stores return in issue
+// order, so the first wait below also covers stores the previous tile's
+// epilogue issued after this tile's first loads.
 template <class C, bool FAST>
 __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, int64_t m0,
-                                              int64_t n0, int wave, int lane,
+                                              int64_t n0, int ph, bool chain, int64_t m1,
+                                              int64_t n1, bool stored, int wave, int lane,
                                               typename C::Acc (&acc)[C::FN][C::FM]) {
   constexpr int S = C::STAGES;
   constexpr int NS = C::kSteps;
@@ -661,6 +703,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
   const int wn = wave % C::WN, wm = wave / C::WN;
   const int KST = static_cast<int>((a.K + C::BK - 1) / C::BK);  // stages
   Loader<C, FAST> ld(a, n0, m0, wave, lane);
+  auto buf = [&](int st) { return smem + ((ph + st) % S) * C::kStage; };
 
   // fragment addressing: row (MF f + lane % MF), chunk (step SB/16 + lane / MF)
   uint32_t lw[NS], lx[NS];
@@ -680,75 +723,128 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
     for (int j = 0; j < C::FM; ++j) acc[i][j] = typename C::Acc{};
 
   if (KST > 0) {
-    wait_stages<C>(PRO - 1);  // stage 0 landed
+    // stage 0 landed; with `stored`, the previous tile's epilogue issued
+    // kFastStores stores after this tile's first PRO stages, which need not
+    // have completed
+    if (stored && C::kSpread)
+      wait_vm<(PRO - 1) * C::kLoadsPerWave + kFastStores<C>>();
+    else
+      wait_stages<C>(PRO - 1);
     block_barrier();
     Frags<C> f[2];
-    read_frags<C>(f[0], smem, lw[0], lx[0]);
+    read_frags<C>(f[0], buf(0), lw[0], lx[0]);
     // nothing in flight on the LDS / scalar-load counter when the K loop
     // starts, so the row waits inside it are exact
     wait_lds();
-    // Full stages; the last (possibly partial) stage is peeled below.  The
-    // stages that refill a buffer run a separately compiled body (no branch
-    // inside the MFMA stream).
     // Stage st's k-steps run as a head (steps 0 .. NS-2) and a tail (the
     // last step, which opens stage st + 1).  The loop body is one stage's
     // tail followed by the next stage's head, so the fragment reads that
     // cross the loop back edge are always waited for by the tail's barrier
     // and the row waits inside the body are exact.
-    auto refill_of = [&](int st, int& rs, int8_t*& rbuf) {
-      if constexpr (C::kSpread) {
-        rs = min(st + S - 1, KST - 1);  // into the buffer freed just before
-        rbuf = smem + ((st + S - 1) % S) * C::kStage;
+    // A stage refills stage st + S - 1 (spread; st + S otherwise) of this
+    // tile while that exists ("own": addresses from per-tile bases the
+    // compiler keeps across the loop); past the end it loads the next
+    // tile's first stages when chained, else it repeats the last stage
+    // ("ext": addresses from a run-time origin, only in the last stages).
+    auto refill_of = [&](int st) {
+      Refill r;
+      const int rs = C::kSpread ? st + S - 1 : st + S;
+      r.buf = C::kSpread ? buf(st + S - 1) : buf(st);  // freed just before / once the next is open
+      if (rs < KST) {
+        r.n0 = n0; r.m0 = m0; r.s = rs;
+      } else if (chain) {
+        r.n0 = n1; r.m0 = m1; r.s = rs - KST;
       } else {
-        rs = min(st + S, KST - 1);      // into this stage's buffer, once the next is open
-        rbuf = smem + (st % S) * C::kStage;
+        r.n0 = n0; r.m0 = m0; r.s = KST - 1;
       }
+      return r;
     };
-    auto head = [&](int st) {
-      int rs;
-      int8_t* rbuf;
-      refill_of(st, rs, rbuf);
-      stage_steps<C, FAST, true, 0, NS - 1>(ld, f, acc, smem + (st % S) * C::kStage,
-                                            smem + ((st + 1) % S) * C::kStage, lw, lx, rs, rbuf,
-                                            S - 2, wave, lane);
+    auto head = [&](auto ext, int st) {
+      const Refill r = refill_of(st);
+      stage_steps<C, FAST, true, decltype(ext)::value, 0, NS - 1>(ld, f, acc, buf(st), buf(st + 1), lw,
+                                                                 lx, r, S - 2, wave, lane);
     };
-    auto tail = [&](int st) {
-      int rs;
-      int8_t* rbuf;
-      refill_of(st, rs, rbuf);
-      stage_steps<C, FAST, true, NS - 1, NS>(ld, f, acc, smem + (st % S) * C::kStage,
-                                             smem + ((st + 1) % S) * C::kStage, lw, lx, rs, rbuf,
-                                             S - 2, wave, lane);
+    auto tail = [&](auto ext, int st) {
+      const Refill r = refill_of(st);
+      stage_steps<C, FAST, true, decltype(ext)::value, NS - 1, NS>(ld, f, acc, buf(st), buf(st + 1),
+                                                                  lw, lx, r, S - 2, wave, lane);
     };
-    const int nfull = KST - 1;  // full stages; the last one is peeled below
-    if (nfull > 0) {
-      head(0);
-      for (int st = 0; st + 1 < nfull; ++st) {
-        tail(st);
-        head(st + 1);
+    // a tail whose wait also lets the previous epilogue's stores stay in
+    // flight (the next stage was loaded before them)
+    auto tail_xst = [&](int st) {
+      const Refill r = refill_of(st);
+      stage_steps<C, FAST, true, false, NS - 1, NS, true>(ld, f, acc, buf(st), buf(st + 1), lw, lx, r,
+                                                          S - 2, wave, lane);
+    };
+    using Own = std::false_type;
+    using Ext = std::true_type;
+    // stages [0, own_end) refill from this tile
+    const int own_end = KST - (C::kSpread ? S - 1 : S);
+    if constexpr (FAST && C::kSpread) {
+      // every stage is whole: the last one runs as a head and a closing
+      // tail that still issues its refills (the next tile's first stages)
+      if (own_end > 0) head(Own{}, 0); else head(Ext{}, 0);
+      int st = 0;
+      // stages 1 .. S-2 were loaded before the previous tile's epilogue
+      // stores: their waits need not wait for the stores
+      if (stored && own_end >= S - 1) {
+        for (; st < S - 2; ++st) {
+          tail_xst(st);
+          head(Own{}, st + 1);
+        }
       }
-      tail(nfull - 1);
-    }
-    {
-      const int st = KST - 1;
-      const int8_t* cur = smem + (st % S) * C::kStage;
-      const int64_t k0 = static_cast<int64_t>(st) * C::BK;
+      for (; st + 1 < own_end; ++st) {
+        tail(Own{}, st);
+        head(Own{}, st + 1);
+      }
+      if (st + 1 < KST && st < own_end) {
+        tail(Own{}, st);
+        head(Ext{}, st + 1);
+        ++st;
+      }
+      for (; st + 1 < KST; ++st) {
+        tail(Ext{}, st);
+        head(Ext{}, st + 1);
+      }
+      const Refill r = refill_of(KST - 1);
+      stage_steps<C, FAST, false, true, NS - 1, NS>(ld, f, acc, buf(KST - 1), buf(KST), lw, lx, r,
+                                                    S - 2, wave, lane);
+      // repeated stages must land before the buffers are reused; chained
+      // loads are the next tile's
+      if (!chain) wait_vm0();
+    } else {
+      // own-tile refills only (repeats clamp the stage index); the last
+      // (possibly partial) stage is peeled below
+      const int nfull = KST - 1;
+      if (nfull > 0) {
+        head(Own{}, 0);
+        for (int st = 0; st + 1 < nfull; ++st) {
+          tail(Own{}, st);
+          head(Own{}, st + 1);
+        }
+        tail(Own{}, nfull - 1);
+      }
+      {
+        const int st = KST - 1;
+        const int8_t* cur = buf(st);
+        const int64_t k0 = static_cast<int64_t>(st) * C::BK;
 #pragma unroll
-      for (int ks = 0; ks < NS; ++ks) {
-        const int64_t ksk = k0 + ks * SB;
-        if (!FAST && ksk >= a.K) break;
-        sched_fence();
-        wait_lds();
-        if (ks + 1 < NS && (FAST || ksk + SB < a.K))
-          read_frags<C>(f[(ks + 1) & 1], cur, lw[ks + 1], lx[ks + 1]);
-        if (!FAST && ksk + SB > a.K) zero_tail<C>(f[ks & 1], ksk, a.K, lane);
-        sched_fence();
-        mfma_step<C>(f[ks & 1], acc);
+        for (int ks = 0; ks < NS; ++ks) {
+          const int64_t ksk = k0 + ks * SB;
+          if (!FAST && ksk >= a.K) break;
+          sched_fence();
+          wait_lds();
+          if (ks + 1 < NS && (FAST || ksk + SB < a.K))
+            read_frags<C>(f[(ks + 1) & 1], cur, lw[ks + 1], lx[ks + 1]);
+          if (!FAST && ksk + SB > a.K) zero_tail<C>(f[ks & 1], ksk, a.K, lane);
+          sched_fence();
+          mfma_step<C>(f[ks & 1], acc);
+        }
       }
+      // the repeated loads past the last stage must land before the buffers
+      // are reused by a next tile or the workgroup ends
+      wait_vm0();
     }
-    // the duplicate loads past the last stage must land before the buffers
-    // are reused by a next tile or the workgroup ends
-    wait_vm0();
   }
 }
 
@@ -791,17 +887,11 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
     tile_prologue<C, true>(a, smem, m0, n0, wave, lane);
   else
     tile_prologue<C, false>(a, smem, m0, n0, wave, lane);
+  const int KST = static_cast<int>((a.K + C::BK - 1) / C::BK);
+  int ph = 0;       // LDS buffer of the current tile's stage 0
+  bool stored = false;  // see tile_mainloop
   typename C::Acc acc[C::FN][C::FM];
   for (;;) {
-    // opaque per tile: lane- and wave-derived offsets are recomputed for
-    // each tile instead of being hoisted out of the tile loop, where their
-    // registers would be held through every K loop
-    int ln = lane, wv = wave;
-    asm volatile("" : "+v"(ln), "+s"(wv));
-    if (fast)
-      tile_mainloop<C, true>(a, smem, m0, n0, wv, ln, acc);
-    else
-      tile_mainloop<C, false>(a, smem, m0, n0, wv, ln, acc);
     const int tnext = t + static_cast<int>(gridDim.x);
     const bool more = tnext < T;
     int64_t m1 = 0, n1 = 0;
@@ -811,6 +901,23 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
       m1 = static_cast<int64_t>(tm) * C::BM;
       n1 = static_cast<int64_t>(tn) * C::BN;
       fast1 = tile_is_fast<C>(a, m1, n1);
+    }
+    // interior tiles chain: this tile's last refills are the next one's
+    // first stages
+    const bool chain = C::kSpread && fast && fast1 && KST > 0;
+    // opaque per tile: lane- and wave-derived offsets are recomputed for
+    // each tile instead of being hoisted out of the tile loop, where their
+    // registers would be held through every K loop
+    int ln = lane, wv = wave;
+    asm volatile("" : "+v"(ln), "+s"(wv));
+    if (fast)
+      tile_mainloop<C, true>(a, smem, m0, n0, ph, chain, m1, n1, stored, wv, ln, acc);
+    else
+      tile_mainloop<C, false>(a, smem, m0, n0, ph, false, m1, n1, stored, wv, ln, acc);
+    if (chain) {
+      ph = (ph + KST) % C::STAGES;
+    } else if (more) {
+      ph = 0;
       block_barrier();  // every wave is done reading this tile's LDS buffers
       int ln1 = lane, wv1 = wave;
       asm volatile("" : "+v"(ln1), "+s"(wv1));
@@ -825,6 +932,9 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
       tile_epilogue<C, true, OUT_I32>(a, m0, n0, wv2, ln2, acc);
     else
       tile_epilogue<C, false, OUT_I32>(a, m0, n0, wv2, ln2, acc);
+    // the next tile's first stages went out before these stores; the
+    // interior bf16 epilogue issues exactly kFastStores of them
+    stored = fast && !OUT_I32;
     if (!more) break;
     t = tnext;
     m0 = m1;
