@@ -124,7 +124,7 @@ def test_gelu_quantize_every_finite_bf16_pattern():
 
 # -------------------------------------------------------------------- GEMM --
 GSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
-           (257, 16, 16), (16, 1000, 3072), (129, 257, 144)]
+           (257, 16, 16), (16, 1000, 3072), (129, 257, 144), (3, 200, 12304)]
 
 
 @pytest.mark.parametrize("M,N,K", GSHAPES)
@@ -147,10 +147,14 @@ def test_gemm_i32_extremes_at_max_k():
     a[1::2] = -127
     b = np.full((18, K), 127, np.int8)
     b[::3] = -127
-    got = host(w8.w8a8_gemm_i32(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)))
+    qa, qb = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    got = host(w8.w8a8_gemm_i32(qa, qb))
     want = oracle.gemm_i64(a, b)
     assert np.abs(want).max() == 16129 * K
     assert np.array_equal(got.astype(np.int64), want)
+    for c in range(ncfg()):
+        g = host(w8.w8a8_gemm_ex(qa, None, qb, None, out_int32=True, config=c))
+        assert np.array_equal(g.astype(np.int64), want), w8.w8a8_gemm_config_name(c)
 
 
 @pytest.mark.parametrize("M,N,K", GSHAPES)

@@ -943,6 +943,123 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
   }
 }
 
+// ----------------------------------------------------------- few tokens --
+// A GEMM with a handful of token rows is bound by streaming the weights from
+// HBM once (M = 1 .. 16: 2 .. 32 ops per weight byte).  Each workgroup owns
+// NB blocks of 16 output columns and 16 token rows; its NW waves split K,
+// each loading its weight and activation fragments straight into registers
+// (ST 64-byte K steps in flight per wave, no LDS staging), accumulating with
+// v_mfma_i32_16x16x64_i8, then the waves' partial sums meet in LDS and the
+// first wave runs the epilogue.  grid.y covers M in steps of 16, so any M
+// works (larger M is better served by the tiled kernel).
+//   MFMA 16x16x64 layout: lane l holds row l % 16 of a 16-row operand, K
+//   bytes 16 (l / 16) .. +15 of a 64-byte step; D[i][j] (i: weight row n,
+//   j: token m) sits in lane j + 16 (i / 4), register i % 4.
+template <int NW, int NB, bool OUT_I32, int ST>
+__global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
+  __shared__ v4i part[NW][NB][64];
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16 * NB;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int r = lane % 16, kq = lane / 16;
+  const int64_t steps = (K + 63) / 64;
+  const int64_t per = (steps + NW - 1) / NW;
+  const int64_t s0 = wave * per, s1 = min(steps, s0 + per);
+  const int64_t mr = m0 + r;
+  const bool mrow = mr < M;
+  const int8_t* xrow = a.qx + (mrow ? mr : 0) * K;
+  const int8_t* wrow[NB];
+  bool nrow[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t nr = n0 + 16 * b + r;
+    nrow[b] = nr < N;
+    wrow[b] = a.qw + (nrow[b] ? nr : 0) * K;
+  }
+  v4i acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = v4i{0, 0, 0, 0};
+  for (int64_t c0 = s0; c0 < s1; c0 += ST) {
+    v4i xf[ST], wf[ST][NB];
+#pragma unroll
+    for (int i = 0; i < ST; ++i) {
+      const int64_t k = (c0 + i) * 64 + kq * 16;
+      const bool in = (c0 + i) < s1 && k < K;
+      // out-of-range pieces are loaded from a valid address and zeroed
+      const int64_t kc = in ? k : 0;
+      xf[i] = *reinterpret_cast<const v4i*>(xrow + kc);
+      if (!(in && mrow)) xf[i] = v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        wf[i][b] = *reinterpret_cast<const v4i*>(wrow[b] + kc);
+        if (!(in && nrow[b])) wf[i][b] = v4i{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ST; ++i)
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i][b], xf[i], acc[b], 0, 0, 0);
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) part[wave][b][lane] = acc[b];
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t m = m0 + lane % 16;
+  if (m >= M) return;
+  const int nq = 4 * (lane / 16);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    v4i t = part[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) t += part[w][b][lane];
+    const int64_t nb = n0 + 16 * b + nq;
+    if constexpr (OUT_I32) {
+      int32_t* out = static_cast<int32_t*>(a.out) + m * N + nb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (nb + e < N) out[e] = t[e];
+    } else {
+      const float sx = a.sx[m];
+      uint16_t* out = static_cast<uint16_t*>(a.out) + m * N + nb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (nb + e < N)
+          out[e] = static_cast<uint16_t>(bf16_bits(dequant(t[e], sx, a.sw[nb + e], bias_term(a.bias, nb + e))));
+    }
+  }
+}
+
+template <int NW, int NB, bool I32, int ST>
+hipError_t launch_few_rows_st(const GemmArgs& a, hipStream_t stream) {
+  const int64_t gx = (a.N + 16 * NB - 1) / (16 * NB), gy = (a.M + 15) / 16;
+  if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
+  gemm_few_rows<NW, NB, I32, ST><<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
+                                   dim3(64 * NW), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Steps in flight per wave: the smallest of 1, 2, 3, 4, 6, 8, 12 that covers
+// the wave's share of K (no load is wasted on a step past the share), else
+// a loop of 12-step chunks.
+template <int NW, int NB, bool I32>
+hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
+  const int64_t per = ((a.K + 63) / 64 + NW - 1) / NW;
+  if (per <= 1) return launch_few_rows_st<NW, NB, I32, 1>(a, stream);
+  if (per <= 2) return launch_few_rows_st<NW, NB, I32, 2>(a, stream);
+  if (per <= 3) return launch_few_rows_st<NW, NB, I32, 3>(a, stream);
+  if (per <= 4) return launch_few_rows_st<NW, NB, I32, 4>(a, stream);
+  if (per <= 6) return launch_few_rows_st<NW, NB, I32, 6>(a, stream);
+  if (per <= 8) return launch_few_rows_st<NW, NB, I32, 8>(a, stream);
+  return launch_few_rows_st<NW, NB, I32, 12>(a, stream);
+}
+
+hipError_t launch_few_rows_any(const GemmArgs& a, bool i32, hipStream_t stream) {
+  return i32 ? launch_few_rows<4, 1, true>(a, stream) : launch_few_rows<4, 1, false>(a, stream);
+}
+
 // ------------------------------------------------------- configurations --
 struct ConfigInfo {
   const char* name;
@@ -970,9 +1087,11 @@ const ConfigInfo kConfigs[] = {
     {"bm64_bn64_bk128_s2_mf32", 64, 64, 256, 4, 0.40f},
     {"bm16_bn64_bk128_s2_mf16", 16, 64, 256, 4, 0.15f},
     {"bm256_bn192_bk64_s4_mf32", 256, 192, 256, 1, 0.92f},
+    {"few_rows_splitk4_mf16", 16, 16, 256, 8, 0.10f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
-constexpr int kSkinny = 6;
+constexpr int kSkinny = 6;    // 16-row tiled kernel
+constexpr int kFewRows = 8;   // split-K few-row kernel
 constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
 template <class C, bool I32>
@@ -1012,15 +1131,21 @@ const char* gemm_config_name(int cfg) {
 
 // Per-shape choice: the configuration with the least estimated time, where a
 // configuration's time is (number of full-chip waves of tiles) x (tile area)
-// x (workgroups sharing a CU) / (relative per-CU throughput).  Skinny M
-// (<= 16) takes the narrow tile.
+// x (workgroups sharing a CU) / (relative per-CU throughput).  A handful of
+// tokens (M <= 16) takes the split-K few-row kernel, except a nearly full
+// 16-row block with enough 64-column tiles to give every CU one: there the
+// 16-row tiled kernel, which shares the activations of a tile through LDS,
+// streams the weights faster.
 int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   (void)K;
-  if (M <= 16) return kSkinny;
+  if (M <= 16) {
+    const int64_t tiles = (N + kConfigs[kSkinny].BN - 1) / kConfigs[kSkinny].BN;
+    return (M > 12 && tiles >= kNumCU) ? kSkinny : kFewRows;
+  }
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < kNumConfigs; ++c) {
-    if (c == kSkinny) continue;
+    if (c == kSkinny || c == kFewRows) continue;  // chosen above for M <= 16
     const ConfigInfo& ci = kConfigs[c];
     const double tiles = static_cast<double>((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
     const double slots = static_cast<double>(kNumCU) * ci.wg_per_cu;
@@ -1046,6 +1171,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 5: return launch_cfg_out<C5>(a, out_int32, stream);
     case 6: return launch_cfg_out<C6>(a, out_int32, stream);
     case 7: return launch_cfg_out<C7>(a, out_int32, stream);
+    case 8: return launch_few_rows_any(a, out_int32, stream);
     default: return hipErrorInvalidValue;
   }
 }
