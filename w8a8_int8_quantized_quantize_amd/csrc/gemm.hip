@@ -1131,7 +1131,9 @@ const char* gemm_config_name(int cfg) {
 
 // Per-shape choice: the configuration with the least estimated time, where a
 // configuration's time is (number of full-chip waves of tiles) x (tile area)
-// x (workgroups sharing a CU) / (relative per-CU throughput).  A handful of
+// x (workgroups sharing a CU) / (relative per-CU throughput).  Workgroups
+// share a CU only when there are more tiles than CUs: with fewer, each tile
+// has a CU to itself and small tiles finish sooner.  A handful of
 // tokens (M <= 16) takes the split-K few-row kernel, except a nearly full
 // 16-row block with enough 64-column tiles to give every CU one: there the
 // 16-row tiled kernel, which shares the activations of a tile through LDS,
@@ -1147,11 +1149,12 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   for (int c = 0; c < kNumConfigs; ++c) {
     if (c == kSkinny || c == kFewRows) continue;  // chosen above for M <= 16
     const ConfigInfo& ci = kConfigs[c];
-    const double tiles = static_cast<double>((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
-    const double slots = static_cast<double>(kNumCU) * ci.wg_per_cu;
-    const double waves = static_cast<double>(static_cast<int64_t>((tiles + slots - 1) / slots));
+    const int64_t tiles = ((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
     // workgroups resident on one CU share its matrix-core throughput
-    const double cost = waves * ci.BM * ci.BN * ci.wg_per_cu / ci.rel_speed;
+    const int64_t share = std::min<int64_t>(ci.wg_per_cu, (tiles + kNumCU - 1) / kNumCU);
+    const int64_t slots = static_cast<int64_t>(kNumCU) * share;
+    const double waves = static_cast<double>((tiles + slots - 1) / slots);
+    const double cost = waves * ci.BM * ci.BN * static_cast<double>(share) / ci.rel_speed;
     if (cost < best_cost - 1e-9) {
       best_cost = cost;
       best = c;
