@@ -6,11 +6,12 @@
 // epilogue folds the two scales and the bias, autotuned per GEMM shape.  The
 // paper's kernel targets Ampere tensor cores; this one is designed for CDNA4:
 //
-//  * MFMA v_mfma_i32_32x32x32_i8 (v_mfma_i32_16x16x64_i8 for the skinny
-//    tile).  The weight tile is the MFMA "A" operand and the activation tile
+//  * MFMA v_mfma_i32_32x32x32_i8 (v_mfma_i32_16x16x64_i8 for the 16-row
+//    tiles).  The weight tile is the MFMA "A" operand and the activation tile
 //    the "B" operand, so a result block holds D[n][m]: each lane owns runs of
-//    four consecutive output columns n of one row m, which the epilogue
-//    writes as 8-byte bf16 stores (16 bytes for int32).
+//    four consecutive output columns n of one row m; lanes l and l + 32 hold
+//    the two halves of eight consecutive columns, which the epilogue joins
+//    (v_permlane32_swap) into one 16-byte bf16 store per lane.
 //  * Both operands are K-contiguous ([M,K] and [N,K] row-major), which is what
 //    the MFMA operand layout wants: every lane reads 16 consecutive k of one
 //    row with a single ds_read_b128, no transposes anywhere.
@@ -25,11 +26,19 @@
 //    nothing may stall the wave between MFMAs: fragment reads and refill
 //    loads are woven in one instruction at a time, and every wait uses an
 //    exact vmcnt / lgkmcnt count (see Sched and wait_next_stage).
+//  * Persistent workgroups: the grid is as many workgroups as fit on the
+//    device at once (a multiple of the 8 XCDs); each walks tiles t, t + grid,
+//    ...  Consecutive interior tiles of a workgroup are chained: the refills
+//    of a tile's last stages already load the next tile's first stages, so
+//    the pipeline never drains between tiles and the epilogue's stores
+//    overlap the next tile's loads.
 //  * Tile order: the dispatcher deals workgroups round-robin to the 8 XCDs,
 //    each with its own L2.  Tile ids are remapped so each XCD receives a
 //    contiguous range, walked in groups of 8 M-tiles, so the workgroups
 //    sharing an L2 also share activation and weight panels, and all walk K
 //    in the same order.
+//  * A handful of token rows (M <= 16) is weight-streaming bound and has its
+//    own split-K kernel (gemm_few_rows) with register-direct loads.
 //  * Epilogue in fp32, no contraction: (s_x[m] * s_w[n]) * float(acc) + bias[n],
 //    rounded once to bf16 (v_cvt_pk_bf16_f32, round to nearest even).  The
 //    int32 accumulators never touch memory unless the int32 debug output is
