@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time every GEMM configuration on every workload shape instead")
     ap.add_argument("--sweep-iters", type=int, default=20)
+    ap.add_argument("--compare", action="store_true",
+                    help="per workload shape: fused INT8 linear vs the 'fake INT8' path "
+                         "(quantize, dequantize to bf16, bf16 GEMM) vs a plain bf16 GEMM")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of known size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -260,6 +263,80 @@ def sweep(args, torch, w8, synthetic):
         del wqs
 
 
+def _time_calls(torch, fn, n_iter, n_copy):
+    """Median and min microseconds of fn(i) over n_iter calls (copy i % n_copy);
+    the stream is primed with a GPU sleep so that each event pair brackets GPU
+    work only."""
+    for i in range(3):
+        fn(i % n_copy)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_iter + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(20_000_000)
+    evs[0].record()
+    for i in range(n_iter):
+        fn(i % n_copy)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    ts = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n_iter))
+    return ts[len(ts) // 2], ts[0]
+
+
+def compare(args, torch, w8, synthetic):
+    """The pages' per-GEMM comparison on MI355X.  For each workload shape, from
+    the same bf16 activations, int8 weights + per-channel scales and bf16 bias:
+      int8:  the fused linear (per-token quantize, int8 GEMM, fused epilogue);
+      fake:  the 'fake INT8' forward the pages start from -- the same per-token
+             quantization, then activations and weights dequantized to bf16
+             and a bf16 GEMM (torch / hipBLASLt), bias added by the GEMM;
+      bf16:  a plain bf16 GEMM on the unquantized bf16 weights.
+    Weight copies rotate past the 256 MB last-level cache for every leg."""
+    import torch.nn.functional as F
+    dev = "cuda:0"
+    shapes = [s for k, v in synthetic.CONFIGS.items() if k != "unit" for s in v]
+    for s in shapes:
+        st = synthetic.streams(0, s.config_id, s.layer_id)
+        x = synthetic.activations_bf16(st, s.M, s.K, s.outlier_frac).to(dev)
+        w = torch.from_numpy(synthetic.weights_f32(st, s.N, s.K)).to(dev)
+        b = synthetic.bias_bf16(st, s.N).to(dev)
+        wq, sw = w8.w8a8_quantize_weight(w)
+        wb = w.to(torch.bfloat16)
+        del w
+        n8 = max(1, min(64, -(-600_000_000 // (s.N * s.K))))
+        n16 = max(1, min(64, -(-600_000_000 // (2 * s.N * s.K))))
+        w8s = [(wq, sw)] + [(wq.clone(), sw.clone()) for _ in range(n8 - 1)]
+        wbs = [wb] + [wb.clone() for _ in range(n16 - 1)]
+        y = torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty((w8.w8a8_linear_workspace_bytes(s.M, s.K),), dtype=torch.uint8, device=dev)
+
+        def int8(i):
+            w8.w8a8_linear(x, w8s[i][0], w8s[i][1], b, out=y, workspace=ws)
+
+        def fake(i):
+            q, sx = w8.w8a8_quantize_act(x)
+            xd = (q.float() * sx[:, None]).to(torch.bfloat16)
+            wd = (w8s[i][0].float() * w8s[i][1][:, None]).to(torch.bfloat16)
+            return F.linear(xd, wd, b)
+
+        def bf16(i):
+            return F.linear(x, wbs[i], b)
+
+        t8 = _time_calls(torch, int8, args.sweep_iters, n8)
+        tf = _time_calls(torch, fake, args.sweep_iters, n8)
+        tb = _time_calls(torch, bf16, args.sweep_iters, n16)
+        int8(0)
+        yf = fake(0)
+        cos = F.cosine_similarity(y.float().flatten(), yf.float().flatten(), dim=0).item()
+        ops = 2.0 * s.M * s.N * s.K
+        print(json.dumps({"compare": s.name, "M": s.M, "K": s.K, "N": s.N,
+                          "int8_fused_us": round(t8[0], 2), "fake_int8_us": round(tf[0], 2),
+                          "bf16_us": round(tb[0], 2),
+                          "int8_TOPS": round(ops / t8[0] / 1e6, 1), "bf16_TFLOPS": round(ops / tb[0] / 1e6, 1),
+                          "speedup_vs_fake_int8": round(tf[0] / t8[0], 2),
+                          "speedup_vs_bf16": round(tb[0] / t8[0], 2),
+                          "cos_int8_vs_fake": round(cos, 6)}), flush=True)
+        del w8s, wbs, ws, y, x, wq, sw, wb
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -285,6 +362,9 @@ def main():
         return 0
     if args.sweep:
         sweep(args, torch, w8, synthetic)
+        return 0
+    if args.compare:
+        compare(args, torch, w8, synthetic)
         return 0
 
     up, down, inp = make_inputs(torch, w8, synthetic, args.rotate)
