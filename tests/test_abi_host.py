@@ -119,3 +119,21 @@ def test_python_binding_rejects_cpu_tensors():
         w8.w8a8_quantize_act(x)
     with pytest.raises(TypeError):
         w8.w8a8_gemm_i32(torch.zeros((4, 16), dtype=torch.int8), torch.zeros((4, 16), dtype=torch.int8))
+
+
+def test_module_swap_host_checks():
+    import torch
+    with pytest.raises(ValueError):
+        w8.W8A8Linear(torch.zeros((4, 16), dtype=torch.float32), torch.ones(4))
+    m = w8.W8A8Linear(torch.zeros((8, 32), dtype=torch.int8), torch.ones(8))
+    assert (m.in_features, m.out_features) == (32, 8) and m.bias is None
+    assert set(m.state_dict()) == {"w_q", "s_w"}
+    # a CPU model: layers the library takes are refused (no CPU path) ...
+    cpu = torch.nn.Sequential(torch.nn.Linear(32, 64), torch.nn.GELU(), torch.nn.Linear(64, 8))
+    with pytest.raises(ValueError, match="not on a GPU"):
+        w8.quantize_linears(cpu)
+    # ... layers it does not take (K % 16 != 0) are left alone, as is a filtered-out one
+    odd = torch.nn.Sequential(torch.nn.Linear(24, 8), torch.nn.Linear(8, 3))
+    assert w8.quantize_linears(odd) == 0
+    assert w8.quantize_linears(cpu, include=lambda name, lin: False) == 0
+    assert isinstance(cpu[0], torch.nn.Linear)

@@ -298,25 +298,66 @@ def w8a8_gemm_select_config(M: int, N: int, K: int) -> int:
     return int(_lib.w8a8_gemm_select_config(int(M), int(N), int(K)))
 
 
-class W8A8Linear:
-    """Drop-in linear layer: weights quantized once per output channel on the
-    GPU, activations per token at every call, one fused GEMM per call."""
+class W8A8Linear(torch.nn.Module):
+    """Drop-in replacement for a bf16 ``nn.Linear``: weights quantized once per
+    output channel on the GPU, activations per token at every call, one fused
+    int8 GEMM with the dequant/bias epilogue per call (the layer the paper
+    swaps into the model's linears, Abstract).  The quantized weights, their
+    scales and the bf16 bias are buffers, so ``state_dict()`` exports them and
+    ``load_state_dict`` restores them.  Inputs must be bf16 on the GPU; leading
+    dimensions are flattened to tokens."""
 
     def __init__(self, w_q: torch.Tensor, s_w: torch.Tensor, bias: torch.Tensor | None = None):
-        self.w_q, self.s_w, self.bias = w_q, s_w, bias
+        super().__init__()
+        if w_q.dtype != torch.int8 or w_q.dim() != 2:
+            raise ValueError("w_q must be an int8 [N, K] tensor")
+        self.out_features, self.in_features = int(w_q.shape[0]), int(w_q.shape[1])
+        self.register_buffer("w_q", w_q)
+        self.register_buffer("s_w", s_w)
+        self.register_buffer("bias", bias)
         self._ws = None
 
     @classmethod
     def from_float(cls, weight: torch.Tensor, bias: torch.Tensor | None = None) -> "W8A8Linear":
-        w_q, s_w = w8a8_quantize_weight(weight.float().contiguous())
-        b = bias.to(torch.bfloat16).contiguous() if bias is not None else None
+        """Quantize a float weight [N, K] (and take a bias) already on the GPU."""
+        w_q, s_w = w8a8_quantize_weight(weight.detach().float().contiguous())
+        b = bias.detach().to(torch.bfloat16).contiguous() if bias is not None else None
         return cls(w_q, s_w, b)
 
-    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+    @classmethod
+    def from_linear(cls, linear: torch.nn.Linear) -> "W8A8Linear":
+        return cls.from_float(linear.weight, linear.bias)
+
+    def extra_repr(self) -> str:
+        return (f"in_features={self.in_features}, out_features={self.out_features}, "
+                f"bias={self.bias is not None}")
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
         need = w8a8_linear_workspace_bytes(x2.shape[0], x2.shape[1])
         if self._ws is None or self._ws.numel() < need or self._ws.device != x2.device:
             self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
         y = w8a8_linear(x2, self.w_q, self.s_w, self.bias, workspace=self._ws)
-        return y.reshape(*lead, self.w_q.shape[0])
+        return y.reshape(*lead, self.out_features)
+
+
+def quantize_linears(module: torch.nn.Module, include=None) -> int:
+    """Replace, in place, every ``nn.Linear`` inside ``module`` whose input
+    width the library takes (a multiple of 16, at most W8A8_MAX_K) by a
+    W8A8Linear quantized from its weights; ``include(name, linear)`` may
+    narrow the choice.  The linears must already be on the GPU.  Returns the
+    number of layers replaced."""
+    count = 0
+    for name, child in list(module.named_children()):
+        if isinstance(child, torch.nn.Linear):
+            k = child.in_features
+            if k % 16 == 0 and 0 < k <= W8A8_MAX_K and (include is None or include(name, child)):
+                if child.weight.device.type != "cuda":
+                    raise ValueError(f"quantize_linears: layer {name!r} is not on a GPU "
+                                     f"(weights are quantized by the library's GPU kernel)")
+                setattr(module, name, W8A8Linear.from_linear(child))
+                count += 1
+        else:
+            count += quantize_linears(child, include)
+    return count
