@@ -190,6 +190,14 @@ def test_linear_k_zero_is_bias_and_empty_batches():
     assert np.array_equal(bits(y), np.tile(bb, (3, 1)))
     y0 = w8.w8a8_linear(x, wq, sw)  # no bias: (s_x * s_w) * 0 = +0
     assert np.all(bits(y0) == 0)
+    # every kernel configuration with K == 0 (no operand bytes exist to load)
+    q0 = torch.zeros((3, 0), dtype=torch.int8, device=DEV)
+    sx0 = torch.ones((3,), dtype=torch.float32, device=DEV)
+    for c in range(ncfg()):
+        yc = w8.w8a8_gemm_ex(q0, sx0, wq, sw, dev_bf16(bb), config=c)
+        assert np.array_equal(bits(yc), np.tile(bb, (3, 1))), w8.w8a8_gemm_config_name(c)
+        gi = w8.w8a8_gemm_ex(q0, None, wq, None, None, out_int32=True, config=c)
+        assert not host(gi).any(), w8.w8a8_gemm_config_name(c)
     # M = 0 and N = 0
     e = w8.w8a8_linear(torch.zeros((0, 32), dtype=torch.bfloat16, device=DEV),
                        torch.zeros((N, 32), dtype=torch.int8, device=DEV), sw)

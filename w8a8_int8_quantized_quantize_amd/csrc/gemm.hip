@@ -964,7 +964,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
 //   MFMA 16x16x64 layout: lane l holds row l % 16 of a 16-row operand, K
 //   bytes 16 (l / 16) .. +15 of a 64-byte step; D[i][j] (i: weight row n,
 //   j: token m) sits in lane j + 16 (i / 4), register i % 4.
-template <int NW, int NB, bool OUT_I32, int ST>
+template <int NW, int NB, bool OUT_I32, int ST, bool LOOP>
 __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
   __shared__ v4i part[NW][NB][64];
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -987,30 +987,65 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
     nrow[b] = nr < N;
     wrow[b] = a.qw + (nrow[b] ? nr : 0) * K;
   }
+  // The epilogue's scales and biases are loaded first, so that their latency
+  // hides behind the weight stream instead of following it.
+  // (Indices are clamped rather than tested, so that the loads are
+  // unconditional and all go out before the first wait.)
+  float sxe = 0.0f, swe[NB][4];
+  uint32_t braw[NB][4];  // bf16 bias bits, widened in the epilogue
+  // (Every wave loads them, though only wave 0 uses them: a branch here
+  // would make the waits after it conservative.)
+  if constexpr (!OUT_I32) {
+    sxe = a.sx[min(m0 + lane % 16, M - 1)];
+    // no bias: read any valid 16-bit word, replaced by -0.0 in the epilogue
+    const uint16_t* bsrc = a.bias ? a.bias : reinterpret_cast<const uint16_t*>(a.sw);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t n = min(n0 + 16 * b + 4 * (lane / 16) + e, N - 1);
+        swe[b][e] = a.sw[n];
+        braw[b][e] = bsrc[n];
+      }
+  }
   v4i acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = v4i{0, 0, 0, 0};
-  for (int64_t c0 = s0; c0 < s1; c0 += ST) {
+  auto chunk = [&](int64_t c0) {
     v4i xf[ST], wf[ST][NB];
+    // Loads only (addresses clamped into the operands): a test on loaded
+    // data here would make each load wait for the one before.  Rows beyond
+    // M or N only feed outputs that are never stored, so they need no
+    // zeroing; steps past the wave's share are skipped below.
 #pragma unroll
     for (int i = 0; i < ST; ++i) {
       const int64_t k = (c0 + i) * 64 + kq * 16;
-      const bool in = (c0 + i) < s1 && k < K;
-      // out-of-range pieces are loaded from a valid address and zeroed
-      const int64_t kc = in ? k : 0;
+      const int64_t kc = ((c0 + i) < s1 && k < K) ? k : 0;
       xf[i] = *reinterpret_cast<const v4i*>(xrow + kc);
-      if (!(in && mrow)) xf[i] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        wf[i][b] = *reinterpret_cast<const v4i*>(wrow[b] + kc);
-        if (!(in && nrow[b])) wf[i][b] = v4i{0, 0, 0, 0};
-      }
+      for (int b = 0; b < NB; ++b) wf[i][b] = *reinterpret_cast<const v4i*>(wrow[b] + kc);
+      __builtin_amdgcn_sched_barrier(0);  // issue order = step order
     }
+    // every load of the chunk is in flight before the first product
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < ST; ++i)
+    for (int i = 0; i < ST; ++i) {
+      if (c0 + i >= s1) break;  // wave-uniform
+      // the 16-byte pieces of a 64-byte step past K (K % 64 != 0) are zeroed
+      const v4i xv = ((c0 + i) * 64 + kq * 16 < K) ? xf[i] : v4i{0, 0, 0, 0};
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i][b], xf[i], acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i][b], xv, acc[b], 0, 0, 0);
+    }
+  };
+  // one chunk covers the wave's share unless it exceeds ST steps; straight
+  // code then (a loop header would make the waits inside it conservative)
+  // (An empty share -- K == 0, or more waves than 64-byte steps -- loads
+  // nothing: with K == 0 the operand pointers need not be valid.)
+  if constexpr (LOOP) {
+    for (int64_t c0 = s0; c0 < s1; c0 += ST) chunk(c0);
+  } else {
+    if (s0 < s1) chunk(s0);
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) part[wave][b][lane] = acc[b];
@@ -1031,22 +1066,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
       for (int e = 0; e < 4; ++e)
         if (nb + e < N) out[e] = t[e];
     } else {
-      const float sx = a.sx[m];
       uint16_t* out = static_cast<uint16_t*>(a.out) + m * N + nb;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (nb + e < N)
-          out[e] = static_cast<uint16_t>(bf16_bits(dequant(t[e], sx, a.sw[nb + e], bias_term(a.bias, nb + e))));
+        if (nb + e < N) {
+          const float bv = a.bias ? __uint_as_float(braw[b][e] << 16) : -0.0f;
+          out[e] = static_cast<uint16_t>(bf16_bits(dequant(t[e], sxe, swe[b][e], bv)));
+        }
     }
   }
 }
 
-template <int NW, int NB, bool I32, int ST>
+template <int NW, int NB, bool I32, int ST, bool LOOP = false>
 hipError_t launch_few_rows_st(const GemmArgs& a, hipStream_t stream) {
   const int64_t gx = (a.N + 16 * NB - 1) / (16 * NB), gy = (a.M + 15) / 16;
   if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
-  gemm_few_rows<NW, NB, I32, ST><<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)),
-                                   dim3(64 * NW), 0, stream>>>(a);
+  gemm_few_rows<NW, NB, I32, ST, LOOP>
+      <<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), dim3(64 * NW), 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -1062,7 +1098,8 @@ hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
   if (per <= 4) return launch_few_rows_st<NW, NB, I32, 4>(a, stream);
   if (per <= 6) return launch_few_rows_st<NW, NB, I32, 6>(a, stream);
   if (per <= 8) return launch_few_rows_st<NW, NB, I32, 8>(a, stream);
-  return launch_few_rows_st<NW, NB, I32, 12>(a, stream);
+  if (per <= 12) return launch_few_rows_st<NW, NB, I32, 12>(a, stream);
+  return launch_few_rows_st<NW, NB, I32, 12, true>(a, stream);
 }
 
 hipError_t launch_few_rows_any(const GemmArgs& a, bool i32, hipStream_t stream) {
