@@ -1067,12 +1067,20 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
         if (nb + e < N) out[e] = t[e];
     } else {
       uint16_t* out = static_cast<uint16_t*>(a.out) + m * N + nb;
+      float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (nb + e < N) {
-          const float bv = a.bias ? __uint_as_float(braw[b][e] << 16) : -0.0f;
-          out[e] = static_cast<uint16_t>(bf16_bits(dequant(t[e], sxe, swe[b][e], bv)));
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float bv = a.bias ? __uint_as_float(braw[b][e] << 16) : -0.0f;
+        v[e] = dequant(t[e], sxe, swe[b][e], bv);
+      }
+      if (N % 4 == 0 && nb + 3 < N) {
+        // the lane's 4 columns in one 8-byte store (rows start 8-byte aligned)
+        *reinterpret_cast<uint2*>(out) = make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nb + e < N) out[e] = static_cast<uint16_t>(bf16_bits(v[e]));
+      }
     }
   }
 }
