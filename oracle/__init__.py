@@ -64,6 +64,12 @@ def lib() -> ctypes.CDLL:
             ("oracle_epilogue", [P, I64, I64, P, P, P, P], ctypes.c_int),
             ("oracle_gelu_f64", [P, P, I64], None),
             ("oracle_gelu_bf16", [P, I64, P], None),
+            ("oracle_e4m3_decode", [P, P, I64], None),
+            ("oracle_e4m3_encode", [P, P, I64], None),
+            ("oracle_quantize_rows_f32_fp8", [P, I64, I64, I64, P, I64, P], None),
+            ("oracle_quantize_rows_bf16_fp8", [P, I64, I64, I64, P, I64, P, P], None),
+            ("oracle_gemm_fp8", [P, I64, P, I64, I64, I64, I64, P], None),
+            ("oracle_epilogue_f64acc", [P, I64, I64, P, P, P, P], None),
         ]:
             fn = getattr(L, name)
             fn.argtypes = args
@@ -178,6 +184,76 @@ def gelu_bf16(y_bits) -> np.ndarray:
     h = np.empty(y.shape, np.uint16)
     lib().oracle_gelu_bf16(_p(y), y.size, _p(h))
     return h
+
+
+# ------------------------------------------------------------ FP8 (e4m3) --
+def e4m3_decode(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().oracle_e4m3_decode(_p(c), _p(out), c.size)
+    return out
+
+
+def e4m3_encode(f) -> np.ndarray:
+    f = _c(f, np.float32)
+    out = np.empty(f.shape, np.uint8)
+    lib().oracle_e4m3_encode(_p(f), _p(out), f.size)
+    return out
+
+
+def quantize_rows_f32_fp8(x):
+    """Per-row e4m3 quantization of fp32 rows -> (codes uint8, scale fp32)."""
+    x = _c(x, np.float32)
+    assert x.ndim == 2
+    R, K = x.shape
+    q = np.empty((R, K), np.uint8)
+    s = np.empty((R,), np.float32)
+    lib().oracle_quantize_rows_f32_fp8(_p(x), R, K, K, _p(q), K, _p(s))
+    return q, s
+
+
+def quantize_rows_bf16_fp8(x_bits):
+    """Per-row (per-token) e4m3 quantization of bf16 rows (uint16 bit patterns)."""
+    x = _c(x_bits, np.uint16)
+    assert x.ndim == 2
+    R, K = x.shape
+    q = np.empty((R, K), np.uint8)
+    s = np.empty((R,), np.float32)
+    tmp = np.empty((R, K), np.float32)
+    lib().oracle_quantize_rows_bf16_fp8(_p(x), R, K, K, _p(q), K, _p(s), _p(tmp))
+    return q, s
+
+
+def gemm_fp8(a, b) -> np.ndarray:
+    """acc[m, n] = sum_k e4m3(a[m, k]) * e4m3(b[n, k]), exact, as fp64."""
+    a = _c(a, np.uint8)
+    b = _c(b, np.uint8)
+    M, K = a.shape
+    N, K2 = b.shape
+    assert K == K2
+    acc = np.empty((M, N), np.float64)
+    lib().oracle_gemm_fp8(_p(a), K, _p(b), K, M, N, K, _p(acc))
+    return acc
+
+
+def epilogue_f64acc(acc, s_x, s_w, bias_bits=None) -> np.ndarray:
+    """bf16 bits of (s_x[m]*s_w[n])*fp32(acc) + bias[n] for an exact fp64 acc."""
+    acc = _c(acc, np.float64)
+    M, N = acc.shape
+    s_x = _c(s_x, np.float32)
+    s_w = _c(s_w, np.float32)
+    y = np.empty((M, N), np.uint16)
+    bias = _c(bias_bits, np.uint16) if bias_bits is not None else None
+    bp = _p(bias) if bias is not None else None
+    lib().oracle_epilogue_f64acc(_p(acc), M, N, _p(s_x), _p(s_w), bp, _p(y))
+    return y
+
+
+def linear_fp8(x_bits, wq, s_w, bias_bits=None):
+    """The FP8 layer: per-token e4m3 quantize -> exact product sums -> epilogue."""
+    q_x, s_x = quantize_rows_bf16_fp8(x_bits)
+    acc = gemm_fp8(q_x, wq)
+    return {"q_x": q_x, "s_x": s_x, "acc": acc, "y": epilogue_f64acc(acc, s_x, s_w, bias_bits)}
 
 
 # ------------------------------------------------------------ composites --

@@ -26,6 +26,20 @@
  *       gelu(v) = v * Phi(v) = 0.5 * v * erfc(-v / sqrt(2)), evaluated in fp64
  *     and rounded once, directly, to bf16.
  *
+ * FP8 variant (the pages' FP8 comparison point; same per-token x per-channel
+ * scheme with OCP e4m3 codes in place of int8), readings:
+ *   - scale = absmax / 448 in fp32 (448 is the largest finite e4m3 value);
+ *     code = e4m3_rne( clamp(fp32 quotient x / scale, -448, 448) ), the
+ *     e4m3 rounding being round-half-to-even on the e4m3 grid (subnormal
+ *     quantum 2^-9); a row whose scale is zero gets all-zero codes;
+ *   - accumulation: the exact sum of the decoded products, computed in fp64
+ *     (a product of two e4m3 values is a multiple of 2^-18 below 2^17.6, so
+ *     for K <= 2^17 every partial sum is an integer multiple of 2^-18 below
+ *     2^53: fp64 holds it exactly), rounded once to fp32 for the epilogue;
+ *   - epilogue: the int8 one, on that fp32 value.  (Matrix cores accumulate
+ *     fp8 products with rounding of their own, so a GPU result is compared
+ *     with this one within a derived error bound, not bit for bit.)
+ *
  * Build: plain C99, -ffp-contract=off, no fast-math, so every float operation
  * below is exactly one IEEE operation.  OpenMP only splits independent rows.
  */
@@ -131,6 +145,110 @@ void oracle_quantize_rows_bf16(const uint16_t* x, int64_t rows, int64_t K, int64
     float* t = tmp_rows + r * K;
     for (int64_t k = 0; k < K; ++k) t[k] = bf16_to_f32(x[r * ldx + k]);
     quantize_row(t, K, q + r * ldq, scale + r);
+  }
+}
+
+/* ------------------------------------------------------ FP8 (e4m3) -- */
+
+/* OCP e4m3 code -> value: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+ * exponent field 0 holds the subnormals m * 2^-9; 0x7F / 0xFF are NaN. */
+static double e4m3_decode(uint8_t c) {
+  int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = e ? ldexp(8.0 + m, e - 10) : ldexp((double)m, -9);
+  return sgn ? -v : v;
+}
+
+/* fp32 value -> OCP e4m3 code, round half to even.  Magnitudes that round
+ * beyond 448 give NaN (no saturation; callers clamp first). */
+static uint8_t e4m3_encode(float f) {
+  if (isnan(f)) return 0x7F;
+  uint8_t sgn = signbit(f) ? 0x80 : 0x00;
+  double a = fabs((double)f);
+  if (a == 0.0) return sgn;
+  int E;
+  frexp(a, &E);            /* a = frac * 2^E, frac in [0.5, 1): a in [2^(E-1), 2^E) */
+  int e = E - 1;           /* unbiased exponent of a */
+  if (e < -6) e = -6;      /* subnormal range shares the quantum of 2^-6 .. 2^-5 */
+  double quantum = ldexp(1.0, e - 3);
+  double r = nearbyint(a / quantum) * quantum;   /* exact division by a power of two */
+  if (r == 0.0) return sgn;
+  if (r > 448.0) return (uint8_t)(sgn | 0x7F);
+  if (r < ldexp(1.0, -6)) return (uint8_t)(sgn | (uint8_t)(r / ldexp(1.0, -9)));  /* subnormal */
+  frexp(r, &E);
+  int er = E - 1;
+  int m = (int)(r / ldexp(1.0, er - 3)) - 8;
+  return (uint8_t)(sgn | ((er + 7) << 3) | m);
+}
+
+void oracle_e4m3_decode(const uint8_t* c, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_decode(c[i]);
+}
+void oracle_e4m3_encode(const float* f, uint8_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(f[i]);
+}
+
+/* One row of fp32 values -> e4m3 codes and one fp32 scale. */
+static void quantize_row_fp8(const float* x, int64_t K, uint8_t* q, float* scale) {
+  float amax = 0.0f;
+  for (int64_t k = 0; k < K; ++k) {
+    float a = fabsf(x[k]);
+    if (a > amax) amax = a;
+  }
+  float s = amax / 448.0f;
+  *scale = s;
+  for (int64_t k = 0; k < K; ++k) {
+    if (s == 0.0f) {
+      q[k] = 0;
+      continue;
+    }
+    float t = x[k] / s;  /* one IEEE fp32 division */
+    if (t > 448.0f) t = 448.0f;
+    if (t < -448.0f) t = -448.0f;
+    q[k] = e4m3_encode(t);
+  }
+}
+
+void oracle_quantize_rows_f32_fp8(const float* x, int64_t rows, int64_t K, int64_t ldx,
+                                  uint8_t* q, int64_t ldq, float* scale) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) quantize_row_fp8(x + r * ldx, K, q + r * ldq, scale + r);
+}
+
+void oracle_quantize_rows_bf16_fp8(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx,
+                                   uint8_t* q, int64_t ldq, float* scale, float* tmp_rows) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float* t = tmp_rows + r * K;
+    for (int64_t k = 0; k < K; ++k) t[k] = bf16_to_f32(x[r * ldx + k]);
+    quantize_row_fp8(t, K, q + r * ldq, scale + r);
+  }
+}
+
+/* acc[m][n] = sum_k decode(a[m][k]) * decode(b[n][k]), exact in fp64 (see header). */
+void oracle_gemm_fp8(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t M,
+                     int64_t N, int64_t K, double* acc) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t n = 0; n < N; ++n) {
+      double sum = 0.0;
+      for (int64_t k = 0; k < K; ++k) sum += e4m3_decode(a[m * lda + k]) * e4m3_decode(b[n * ldb + k]);
+      acc[m * N + n] = sum;
+    }
+  }
+}
+
+/* y = bf16( (s_x[m] * s_w[n]) * fp32(acc) + float(bias[n]) ); bias may be NULL. */
+void oracle_epilogue_f64acc(const double* acc, int64_t M, int64_t N, const float* s_x,
+                            const float* s_w, const uint16_t* bias, uint16_t* y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m) {
+    for (int64_t n = 0; n < N; ++n) {
+      float f = s_x[m] * s_w[n];
+      float v = f * (float)acc[m * N + n];
+      float o = bias ? v + bf16_to_f32(bias[n]) : v;
+      y[m * N + n] = f32_to_bf16(o);
+    }
   }
 }
 
