@@ -172,6 +172,51 @@ int w8a8_gemm_ex(const int8_t* q_x, const float* s_x, const int8_t* w_q, const f
                  const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* out,
                  int out_int32, int config, void* stream);
 
+/*
+ * FP8 variant: the same per-token x per-channel scheme with OCP e4m3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
+ * value 448; bytes 0x7F and 0xFF are NaN) in place of int8 -- the FP8 path
+ * the pages compare the INT8 one with (Abstract; news write-up, third
+ * paragraph).  Same sizes, alignment, leading-dimension, workspace and error
+ * rules as the int8 entry points above.
+ *
+ * Quantization (per token for bf16 activations, per output channel for fp32
+ * weights):  scale = fl32(absmax / 448);  code = e4m3_rne(clamp(fl32(x /
+ * scale), -448, 448)), round half to even on the e4m3 grid (subnormal step
+ * 2^-9); a row whose scale is 0 gets all-zero codes.  Codes are uint8 bytes.
+ */
+int w8a8_quantize_act_fp8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                          int64_t ldq, float* scale, void* stream);
+int w8a8_quantize_weight_fp8(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                             int64_t ldq, float* scale, void* stream);
+
+/*
+ * y[m,n] = bf16_rne((s_x[m] * s_w[n]) * acc[m,n] + bias[n]) with acc the sum
+ * over k of e4m3(q_x[m,k]) * e4m3(w_q[n,k]) accumulated in fp32 on the FP8
+ * matrix cores (their accumulation rounds, so acc matches the exact sum
+ * within a small relative error, not bit for bit).  Codes must be finite (no
+ * NaN bytes); the quantizers above never produce them.  Fastest when K is a
+ * multiple of 128.  config: -1 for the library's choice, else 0 ..
+ * w8a8_gemm_fp8_num_configs() - 1.
+ */
+int w8a8_gemm_dequant_fp8(const uint8_t* q_x, const float* s_x, const uint8_t* w_q,
+                          const float* s_w, const void* bias_bf16, int64_t M, int64_t N, int64_t K,
+                          void* y_bf16, void* stream);
+int w8a8_gemm_fp8_ex(const uint8_t* q_x, const float* s_x, const uint8_t* w_q, const float* s_w,
+                     const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
+                     int config, void* stream);
+int w8a8_gemm_fp8_num_configs(void);
+const char* w8a8_gemm_fp8_config_name(int config);
+
+/*
+ * The fused FP8 linear: w8a8_quantize_act_fp8 of x into the workspace (same
+ * size as w8a8_linear's: w8a8_linear_workspace_bytes(M, K)), then
+ * w8a8_gemm_dequant_fp8.  w_q, s_w from w8a8_quantize_weight_fp8.
+ */
+int w8a8_linear_fp8(const void* x_bf16, const uint8_t* w_q, const float* s_w,
+                    const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

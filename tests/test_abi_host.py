@@ -112,6 +112,33 @@ def test_config_selection_table():
     assert w8.w8a8_gemm_select_config(0, 4, 16) == -1
 
 
+def test_fp8_entry_validation():
+    q = L.w8a8_quantize_act_fp8
+    assert q(None, 0, 16, 16, None, 16, None, None) == OK
+    assert q(A, 4, 17, 17, A, 32, A, None) == SHAPE
+    assert q(A, 4, 16, 16, A, 24, A, None) == ALIGN                 # code row stride 24 B
+    assert q(A, 4, 16, 16, A, 16, None, None) == NULL
+    w = L.w8a8_quantize_weight_fp8
+    assert w(A, 4, 16, 18, A, 16, A, None) == ALIGN                 # fp32 row stride 72 B
+    assert w(A, 4, 133152, 133152, A, 133152, A, None) == KOVF
+    d = L.w8a8_gemm_dequant_fp8
+    assert d(None, None, None, None, None, 0, 4, 16, None, None) == OK
+    assert d(A, None, A, A, None, 4, 4, 16, A, None) == NULL        # s_x
+    assert d(A, A, A, A, P(0x10001), 4, 4, 16, A, None) == ALIGN    # bias
+    assert d(A, A, MIS, A, None, 4, 4, 16, A, None) == ALIGN
+    e = L.w8a8_gemm_fp8_ex
+    n = w8.w8a8_gemm_fp8_num_configs()
+    assert n >= 1 and all(w8.w8a8_gemm_fp8_config_name(i) for i in range(n))
+    assert w8.w8a8_gemm_fp8_config_name(n) is None
+    assert e(A, A, A, A, None, 4, 4, 16, A, n, None) == CFG
+    assert e(A, A, A, A, None, 4, 4, 16, A, -2, None) == CFG
+    lin = L.w8a8_linear_fp8
+    need = w8.w8a8_linear_workspace_bytes(4, 16)
+    assert lin(A, A, A, None, 4, 4, 16, A, A, need - 1, None) == WS
+    assert lin(A, A, A, None, 4, 4, 17, A, A, need, None) == SHAPE
+    assert lin(None, None, None, None, 0, 4, 16, None, None, 0, None) == OK
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     x = torch.zeros((4, 16), dtype=torch.bfloat16)

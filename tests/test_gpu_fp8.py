@@ -1,0 +1,159 @@
+"""Parity of the FP8 (OCP e4m3) path with the oracle.
+
+Quantization (codes and scales) is deterministic and compared bit for bit.
+The GEMM accumulates e4m3 products on the matrix cores in fp32 with rounding
+of their own, so its bf16 output is compared with the oracle's (built on the
+exact sum of products) within a derived bound:
+    |y_gpu - y_exact| <= |s_x s_w| * 2^-12 * sum_k |a_k b_k|  +  1 bf16 ulp of y,
+where 2^-12 covers the matrix cores' accumulation error (measured on this
+hardware at up to 2^-13.5 of sum |a_k b_k| for one 64-deep product, with
+fp32 additions across steps adding at most K/64 * 2^-24 relative) and the
+ulp covers the final rounding.  Cosine >= 0.99999 against the oracle and no
+NaN/Inf are required as well.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+import w8a8_int8_quantized_quantize_amd as w8
+from gpu_helpers import DEV, bits, cosine, dev_bf16, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+EPS_ACC = 2.0 ** -12
+
+
+def rand_bits(rng, M, K, scale=1.0, outliers=0):
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.float32(scale)
+    if outliers:
+        x[:, rng.permutation(K)[:outliers]] *= np.float32(20.0)
+    return synthetic.bf16_bits(synthetic.bf16_from_f32(x))
+
+
+def bf16_vals(b: np.ndarray) -> np.ndarray:
+    return oracle.bf16_to_f32(b).astype(np.float64)
+
+
+def assert_fp8_gemm_bound(y_bits, q_x, s_x, q_w, s_w, bias_bits, what=""):
+    acc = oracle.gemm_fp8(q_x, q_w)
+    mag = oracle.gemm_fp8(q_x & 0x7F, q_w & 0x7F)  # sum_k |a_k b_k|, exact
+    f = s_x.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :]
+    yv = f * acc + (bf16_vals(bias_bits)[None, :] if bias_bits is not None else 0.0)
+    got = bf16_vals(y_bits)
+    assert np.all(np.isfinite(got)), what
+    tol = np.abs(f) * EPS_ACC * mag + np.abs(yv) * 2.0 ** -8 + 1e-30
+    err = np.abs(got - yv)
+    assert np.all(err <= tol), (what, float((err / tol).max()))
+    want = oracle.epilogue_f64acc(acc, s_x, s_w, bias_bits)
+    assert cosine(y_bits, want) >= 0.99999, what
+    return float(np.mean(y_bits != want))
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (7, 48), (33, 1040), (64, 256), (257, 3072), (5, 12288)])
+def test_quantize_act_fp8_bit_exact(M, K):
+    rng = np.random.default_rng(M * 13 + K)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    if M > 2:
+        xb[1] = 0
+        xb[2] = rand_bits(rng, 1, K, scale=1e-39)[0]
+    q, s = w8.w8a8_quantize_act_fp8(dev_bf16(xb))
+    qo, so = oracle.quantize_rows_bf16_fp8(xb)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+def test_quantize_act_fp8_ties_and_clamp():
+    # scale 1 rows (absmax 448) holding e4m3 ties, and a row whose tiny scale
+    # pushes quotients past 448
+    vals = np.array([448, 1.0625, 1.1875, -1.0625, 0.0009765625, -0.0029296875, 3.25, 6.5] * 8,
+                    np.float32)
+    x = np.tile(vals, (3, 1))
+    x[2] = np.float32(2.0 ** -126) * np.linspace(-1, 1, x.shape[1]).astype(np.float32)
+    xb = synthetic.bf16_bits(synthetic.bf16_from_f32(x))
+    q, s = w8.w8a8_quantize_act_fp8(dev_bf16(xb))
+    qo, so = oracle.quantize_rows_bf16_fp8(xb)
+    assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
+    assert host(q)[0, :4].tolist() == [0x7E, 0x38, 0x3A, 0xB8]
+
+
+@pytest.mark.parametrize("N,K", [(128, 256), (300, 1040), (64, 12288), (3, 16)])
+def test_quantize_weight_fp8_bit_exact(N, K):
+    rng = np.random.default_rng(N + 7 * K)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if N > 2:
+        w[1] = 0
+        w[2] = np.float32(2.0 ** -149) * rng.integers(-200, 200, K).astype(np.float32)
+    q, s = w8.w8a8_quantize_weight_fp8(torch.from_numpy(w).to(DEV))
+    qo, so = oracle.quantize_rows_f32_fp8(w)
+    assert np.array_equal(host(s).view(np.uint32), so.view(np.uint32))
+    assert np.array_equal(host(q), qo)
+
+
+FSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
+           (257, 136, 384), (129, 257, 3072)]
+
+
+@pytest.mark.parametrize("M,N,K", FSHAPES)
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gemm_fp8_every_config_within_bound(M, N, K, with_bias):
+    rng = np.random.default_rng(M + 3 * N + K + with_bias)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0] if with_bias else None
+    qx, sx = oracle.quantize_rows_bf16_fp8(xb)
+    qw, sw = oracle.quantize_rows_f32_fp8(w)
+    dq, dsx = torch.from_numpy(qx).to(DEV), torch.from_numpy(sx).to(DEV)
+    dw, dsw = torch.from_numpy(qw).to(DEV), torch.from_numpy(sw).to(DEV)
+    bias = dev_bf16(bb) if with_bias else None
+    ys = []
+    for c in range(w8.w8a8_gemm_fp8_num_configs()):
+        y = bits(w8.w8a8_gemm_dequant_fp8(dq, dsx, dw, dsw, bias, config=c))
+        assert_fp8_gemm_bound(y, qx, sx, qw, sw, bb, f"{M}x{N}x{K} {w8.w8a8_gemm_fp8_config_name(c)}")
+        ys.append(y)
+    # the fused entry: quantize + GEMM, same codes as the oracle's
+    y = bits(w8.w8a8_linear_fp8(dev_bf16(xb), dw, dsw, bias))
+    assert_fp8_gemm_bound(y, qx, sx, qw, sw, bb, f"linear {M}x{N}x{K}")
+
+
+def test_gemm_fp8_extremes_and_k_zero():
+    # all codes +-448: sums of 448^2 products (exact in fp32 up to K = 256)
+    M, N, K = 40, 72, 256
+    a = np.full((M, K), 0x7E, np.uint8)
+    a[1::2] = 0xFE
+    b = np.full((N, K), 0x7E, np.uint8)
+    ones = torch.ones((M,), dtype=torch.float32, device=DEV)
+    onesn = torch.ones((N,), dtype=torch.float32, device=DEV)
+    for c in range(w8.w8a8_gemm_fp8_num_configs()):
+        y = w8.w8a8_gemm_dequant_fp8(torch.from_numpy(a).to(DEV), ones, torch.from_numpy(b).to(DEV),
+                                     onesn, config=c)
+        want = np.where(np.arange(M)[:, None] % 2 == 1, -448.0 * 448 * K, 448.0 * 448 * K)
+        assert np.array_equal(host(y.float()), np.broadcast_to(want, (M, N)).astype(np.float32)), c
+    # K == 0: output is the bias
+    bb = rand_bits(np.random.default_rng(9), 1, N, scale=0.1)[0]
+    q0 = torch.zeros((M, 0), dtype=torch.uint8, device=DEV)
+    w0 = torch.zeros((N, 0), dtype=torch.uint8, device=DEV)
+    for c in range(w8.w8a8_gemm_fp8_num_configs()):
+        y = w8.w8a8_gemm_dequant_fp8(q0, ones, w0, onesn, dev_bf16(bb), config=c)
+        assert np.array_equal(bits(y), np.tile(bb, (M, 1))), c
+
+
+@pytest.mark.parametrize("shape", [s for s in synthetic.CONFIGS["dit1024_mlp"]] +
+                         [synthetic.CONFIGS["dit768_attn"][1]], ids=lambda s: s.name)
+def test_full_size_linear_fp8_sampled(shape):
+    st = synthetic.streams(0, shape.config_id, shape.layer_id)
+    x = synthetic.activations_bf16(st, shape.M, shape.K, shape.outlier_frac)
+    w = synthetic.weights_f32(st, shape.N, shape.K)
+    b = synthetic.bias_bf16(st, shape.N)
+    dwq, dsw = w8.w8a8_quantize_weight_fp8(torch.from_numpy(w).to(DEV))
+    qw, sw = oracle.quantize_rows_f32_fp8(w)
+    assert np.array_equal(host(dwq), qw) and np.array_equal(host(dsw), sw)
+    y = w8.w8a8_linear_fp8(x.to(DEV), dwq, dsw, b.to(DEV))
+    rows = sample_rows(shape.M, 16)
+    xb = synthetic.bf16_bits(x)[rows]
+    bb = synthetic.bf16_bits(b)
+    qx, sx = oracle.quantize_rows_bf16_fp8(xb)
+    assert_fp8_gemm_bound(bits(y)[rows], qx, sx, qw, sw, bb, shape.name)

@@ -54,6 +54,13 @@ def _load() -> ctypes.CDLL:
         "w8a8_gemm_config_name": ([I], ctypes.c_char_p),
         "w8a8_gemm_select_config": ([I64, I64, I64], I),
         "w8a8_gemm_ex": ([P, P, P, P, P, I64, I64, I64, P, I, I, P], I),
+        "w8a8_quantize_act_fp8": ([P, I64, I64, I64, P, I64, P, P], I),
+        "w8a8_quantize_weight_fp8": ([P, I64, I64, I64, P, I64, P, P], I),
+        "w8a8_gemm_dequant_fp8": ([P, P, P, P, P, I64, I64, I64, P, P], I),
+        "w8a8_gemm_fp8_ex": ([P, P, P, P, P, I64, I64, I64, P, I, P], I),
+        "w8a8_gemm_fp8_num_configs": ([], I),
+        "w8a8_gemm_fp8_config_name": ([I], ctypes.c_char_p),
+        "w8a8_linear_fp8": ([P, P, P, P, I64, I64, I64, P, P, ctypes.c_size_t, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -296,6 +303,102 @@ def w8a8_gemm_config_name(config: int) -> str | None:
 
 def w8a8_gemm_select_config(M: int, N: int, K: int) -> int:
     return int(_lib.w8a8_gemm_select_config(int(M), int(N), int(K)))
+
+
+# ------------------------------------------------------------------ FP8 --
+# OCP e4m3 codes travel as uint8 tensors (view them as torch.float8_e4m3fn
+# for their values).
+def _quantize_rows_fp8(fn, x, dtype, q, scale, what):
+    _need(x, what, dtype, 2)
+    R, K = x.shape
+    q = torch.empty((R, K), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty((R,), dtype=torch.float32, device=x.device) if scale is None else scale
+    _need(q, "q", torch.uint8, 2)
+    _need(scale, "scale", torch.float32, 1)
+    _same_device(x, q, scale)
+    if tuple(q.shape) != (R, K) or tuple(scale.shape) != (R,) or not scale.is_contiguous():
+        raise ValueError(f"output shapes do not match {what}")
+    rc = getattr(_lib, fn)(_ptr(x), R, K, _rows(x, what), _ptr(q), _rows(q, "q"), _ptr(scale),
+                           _stream(x.device))
+    _check(rc, fn)
+    return q, scale
+
+
+def w8a8_quantize_act_fp8(x, q=None, scale=None):
+    """Per-token e4m3 quantization: bf16 [M, K] -> (uint8 codes [M, K], fp32 [M])."""
+    return _quantize_rows_fp8("w8a8_quantize_act_fp8", x, torch.bfloat16, q, scale, "x")
+
+
+def w8a8_quantize_weight_fp8(w, q=None, scale=None):
+    """Per-output-channel e4m3 quantization: fp32 [N, K] -> (uint8 codes [N, K], fp32 [N])."""
+    return _quantize_rows_fp8("w8a8_quantize_weight_fp8", w, torch.float32, q, scale, "w")
+
+
+def w8a8_gemm_dequant_fp8(q_x, s_x, w_q, s_w, bias=None, out=None, config=-1):
+    """e4m3 GEMM (fp32 accumulation) + dequant/bias epilogue -> bf16 [M, N];
+    config -1 is the library's choice."""
+    _need(q_x, "q_x", torch.uint8, 2)
+    _need(w_q, "w_q", torch.uint8, 2)
+    M, K = q_x.shape
+    N, K2 = w_q.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: q_x {tuple(q_x.shape)} vs w_q {tuple(w_q.shape)}")
+    if not (q_x.is_contiguous() and w_q.is_contiguous()):
+        raise ValueError("q_x and w_q must be contiguous")
+    _vec(s_x, "s_x", torch.float32, M)
+    _vec(s_w, "s_w", torch.float32, N)
+    _vec(bias, "bias", torch.bfloat16, N)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=q_x.device) if out is None else out
+    _need(out, "out", torch.bfloat16, 2)
+    _same_device(q_x, s_x, w_q, s_w, bias, out)
+    if tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] bf16 tensor")
+    rc = _lib.w8a8_gemm_fp8_ex(_ptr(q_x), _ptr(s_x), _ptr(w_q), _ptr(s_w), _ptr(bias), M, N, K,
+                               _ptr(out), int(config), _stream(q_x.device))
+    _check(rc, "w8a8_gemm_fp8_ex")
+    return out
+
+
+def w8a8_gemm_fp8_ex(q_x, s_x, w_q, s_w, bias=None, out=None, config=-1):
+    """Same as w8a8_gemm_dequant_fp8 (the C entry with an explicit configuration)."""
+    return w8a8_gemm_dequant_fp8(q_x, s_x, w_q, s_w, bias, out, config)
+
+
+def w8a8_linear_fp8(x, w_q, s_w, bias=None, out=None, workspace=None):
+    """The fused FP8 linear: bf16 x [M, K] -> bf16 y [M, N] (w_q, s_w from
+    w8a8_quantize_weight_fp8; workspace as for w8a8_linear)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_q, "w_q", torch.uint8, 2)
+    M, K = x.shape
+    N, K2 = w_q.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)} vs w_q {tuple(w_q.shape)}")
+    if not (x.is_contiguous() and w_q.is_contiguous()):
+        raise ValueError("x and w_q must be contiguous")
+    _vec(s_w, "s_w", torch.float32, N)
+    _vec(bias, "bias", torch.bfloat16, N)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] bf16 tensor")
+    need = w8a8_linear_workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(x, w_q, s_w, bias, out, workspace)
+    rc = _lib.w8a8_linear_fp8(_ptr(x), _ptr(w_q), _ptr(s_w), _ptr(bias), M, N, K, _ptr(out),
+                              _ptr(workspace), workspace.numel(), _stream(x.device))
+    _check(rc, "w8a8_linear_fp8")
+    return out
+
+
+def w8a8_gemm_fp8_num_configs() -> int:
+    return int(_lib.w8a8_gemm_fp8_num_configs())
+
+
+def w8a8_gemm_fp8_config_name(config: int) -> str | None:
+    r = _lib.w8a8_gemm_fp8_config_name(int(config))
+    return r.decode() if r else None
 
 
 class W8A8Linear(torch.nn.Module):

@@ -91,6 +91,29 @@ int gemm_any(const int8_t* q_x, const float* s_x, const int8_t* w_q, const float
   return hip_status(w8a8::launch_gemm(a, out_i32, cfg, as_stream(stream)));
 }
 
+int gemm_fp8_any(const uint8_t* q_x, const float* s_x, const uint8_t* w_q, const float* s_w,
+                 const void* bias, int64_t M, int64_t N, int64_t K, void* y, int config,
+                 void* stream) {
+  const int8_t* qx = reinterpret_cast<const int8_t*>(q_x);
+  const int8_t* qw = reinterpret_cast<const int8_t*>(w_q);
+  if (int rc = check_gemm(qx, qw, M, N, K, y)) return rc;
+  if (int rc = check_dequant(s_x, s_w, bias, M, N)) return rc;
+  if (config < -1 || config >= w8a8::gemm_fp8_num_configs()) return W8A8_ERR_CONFIG;
+  if (M == 0 || N == 0) return W8A8_OK;
+  const int cfg = config >= 0 ? config : w8a8::gemm_fp8_select_config(M, N, K);
+  GemmArgs a;
+  a.qx = qx;
+  a.qw = qw;
+  a.sx = s_x;
+  a.sw = s_w;
+  a.bias = static_cast<const uint16_t*>(bias);
+  a.out = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return hip_status(w8a8::launch_gemm_fp8(a, cfg, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -178,6 +201,63 @@ int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w, const v
     return rc;
   return gemm_any(qx, sx, w_q, s_w, bias_bf16, M, N, K, y_bf16, false, -1, stream);
 }
+
+int w8a8_quantize_act_fp8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
+                          int64_t ldq, float* scale, void* stream) {
+  int8_t* qb = reinterpret_cast<int8_t*>(q);
+  if (int rc = check_rows(x_bf16, M, K, ldx, 2, qb, ldq, scale)) return rc;
+  if (M == 0) return W8A8_OK;
+  return hip_status(w8a8::launch_quantize_rows(QuantSrc::kBf16Fp8, x_bf16, M, K, ldx, qb, ldq,
+                                               scale, nullptr, as_stream(stream)));
+}
+
+int w8a8_quantize_weight_fp8(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
+                             int64_t ldq, float* scale, void* stream) {
+  int8_t* qb = reinterpret_cast<int8_t*>(q);
+  if (int rc = check_rows(w, N, K, ldw, 4, qb, ldq, scale)) return rc;
+  if (N == 0) return W8A8_OK;
+  return hip_status(w8a8::launch_quantize_rows(QuantSrc::kF32Fp8, w, N, K, ldw, qb, ldq, scale,
+                                               nullptr, as_stream(stream)));
+}
+
+int w8a8_gemm_dequant_fp8(const uint8_t* q_x, const float* s_x, const uint8_t* w_q,
+                          const float* s_w, const void* bias_bf16, int64_t M, int64_t N, int64_t K,
+                          void* y_bf16, void* stream) {
+  return gemm_fp8_any(q_x, s_x, w_q, s_w, bias_bf16, M, N, K, y_bf16, -1, stream);
+}
+
+int w8a8_gemm_fp8_ex(const uint8_t* q_x, const float* s_x, const uint8_t* w_q, const float* s_w,
+                     const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
+                     int config, void* stream) {
+  return gemm_fp8_any(q_x, s_x, w_q, s_w, bias_bf16, M, N, K, y_bf16, config, stream);
+}
+
+int w8a8_linear_fp8(const void* x_bf16, const uint8_t* w_q, const float* s_w,
+                    const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0) return W8A8_ERR_SHAPE;
+  if (int rc = check_k(K)) return rc;
+  if (M == 0 || N == 0) return W8A8_OK;
+  const size_t need = w8a8_linear_workspace_bytes(M, K);
+  if (workspace == nullptr || workspace_bytes < need) return W8A8_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return W8A8_ERR_ALIGN;
+  int8_t* qx = static_cast<int8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       pad(static_cast<size_t>(M) * static_cast<size_t>(K)));
+  // validate both stages before enqueueing either
+  if (int rc = check_rows(x_bf16, M, K, K, 2, qx, K, sx)) return rc;
+  if (int rc = check_gemm(qx, reinterpret_cast<const int8_t*>(w_q), M, N, K, y_bf16)) return rc;
+  if (int rc = check_dequant(sx, s_w, bias_bf16, M, N)) return rc;
+  if (int rc = hip_status(w8a8::launch_quantize_rows(QuantSrc::kBf16Fp8, x_bf16, M, K, K, qx, K,
+                                                     sx, nullptr, as_stream(stream))))
+    return rc;
+  return gemm_fp8_any(reinterpret_cast<const uint8_t*>(qx), sx, w_q, s_w, bias_bf16, M, N, K,
+                      y_bf16, -1, stream);
+}
+
+int w8a8_gemm_fp8_num_configs(void) { return w8a8::gemm_fp8_num_configs(); }
+
+const char* w8a8_gemm_fp8_config_name(int config) { return w8a8::gemm_fp8_config_name(config); }
 
 int w8a8_gemm_num_configs(void) { return w8a8::gemm_num_configs(); }
 

@@ -56,7 +56,9 @@ namespace w8a8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) int8_t global_i8;
 
@@ -81,30 +83,48 @@ __device__ __forceinline__ int swz(int r, int c) {
 // MF = 16: v_mfma_i32_16x16x64_i8, 64 bytes of K per step; lane l holds row
 // l % 16, K bytes 16 (l / 16) .. +15, and D[i][j] sits in lane j + 16 (i / 4),
 // register i % 4.
-template <int MF>
+template <int MF, bool FP8 = false>
 struct Mfma;
+// kStepBytes: K bytes of one MFMA; Frag: one lane's operand, read from LDS
+// as kReads 16-byte pieces.
 template <>
-struct Mfma<32> {
+struct Mfma<32, false> {
   using Acc = v16i;
-  static constexpr int kStepBytes = 32, kGroups = 4;
-  static __device__ __forceinline__ Acc run(v4i a, v4i b, Acc c) {
+  using Frag = v4i;
+  static constexpr int kStepBytes = 32, kGroups = 4, kReads = 1;
+  static __device__ __forceinline__ Acc run(Frag a, Frag b, Acc c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
   }
 };
 template <>
-struct Mfma<16> {
+struct Mfma<16, false> {
   using Acc = v4i;
-  static constexpr int kStepBytes = 64, kGroups = 1;
-  static __device__ __forceinline__ Acc run(v4i a, v4i b, Acc c) {
+  using Frag = v4i;
+  static constexpr int kStepBytes = 64, kGroups = 1, kReads = 1;
+  static __device__ __forceinline__ Acc run(Frag a, Frag b, Acc c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
   }
 };
+// FP8 (OCP e4m3) operands, fp32 accumulation: v_mfma_scale_f32_32x32x64_f8f6f4
+// with both block scales 2^0 (E8M0 code 127) and e4m3 for both operands.  Same
+// result layout as the int8 32x32 MFMA; a lane supplies 32 consecutive K
+// bytes of its row (two 16-byte LDS reads).
+template <>
+struct Mfma<32, true> {
+  using Acc = v16f;
+  using Frag = v8i;
+  static constexpr int kStepBytes = 64, kGroups = 4, kReads = 2;
+  static __device__ __forceinline__ Acc run(Frag a, Frag b, Acc c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int MF_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int MF_, bool FP8_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
   static constexpr int MF = MF_;
-  using Op = Mfma<MF>;
+  static constexpr bool kFp8 = FP8_;
+  using Op = Mfma<MF, FP8_>;
   using Acc = typename Op::Acc;
   static constexpr int kSlots = BK / 16;            // 16-byte chunks per LDS row
   static constexpr int kSteps = BK / Op::kStepBytes;
@@ -293,22 +313,35 @@ struct Loader {
 
 template <class C>
 struct Frags {
-  v4i w[C::FN];
-  v4i x[C::FM];
+  typename C::Op::Frag w[C::FN];
+  typename C::Op::Frag x[C::FM];
 };
+
+// One lane's operand at byte offset `off` of an LDS stage.  A two-piece
+// (32-byte) operand is the logical 16-byte chunks 2c and 2c + 1 of its row;
+// the chunk swizzle is an XOR on the chunk index, so their slots differ only
+// in the lowest bit: offsets off and off ^ 16.
+template <class C>
+__device__ __forceinline__ typename C::Op::Frag load_frag(const int8_t* stage, uint32_t off) {
+  if constexpr (C::Op::kReads == 1) {
+    return *reinterpret_cast<const v4i*>(stage + off);
+  } else {
+    const v4i lo = *reinterpret_cast<const v4i*>(stage + off);
+    const v4i hi = *reinterpret_cast<const v4i*>(stage + (off ^ 16u));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
 
 // Fragments of one k-step: lane reads row (MF f + lane % MF) of its wave tile
 // at the lane's chunk; lw / lx: lane + wave part of the address.
 template <class C>
 __device__ __forceinline__ void read_frags(Frags<C>& fr, const int8_t* stage, uint32_t lw,
                                            uint32_t lx) {
-  const int8_t* sw = stage + lw;
-  const int8_t* sx = stage + lx;
   // same order as the interleaved schedule: activation fragments first
 #pragma unroll
-  for (int f = 0; f < C::FM; ++f) fr.x[f] = *reinterpret_cast<const v4i*>(sx + f * C::MF * C::BK);
+  for (int f = 0; f < C::FM; ++f) fr.x[f] = load_frag<C>(stage, lx + f * C::MF * C::BK);
 #pragma unroll
-  for (int f = 0; f < C::FN; ++f) fr.w[f] = *reinterpret_cast<const v4i*>(sw + f * C::MF * C::BK);
+  for (int f = 0; f < C::FN; ++f) fr.w[f] = load_frag<C>(stage, lw + f * C::MF * C::BK);
 }
 
 // MFMAs of one k-step, weight-fragment rows [I0, I1).
@@ -355,6 +388,12 @@ __device__ __forceinline__ float bias_term(const uint16_t* bias, int64_t n) {
 __device__ __forceinline__ float dequant(int32_t acc, float sx, float sw, float b) {
   const float f = sx * sw;
   const float v = f * static_cast<float>(acc);
+  return v + b;
+}
+// fp32 accumulator (FP8 operands): the same order without the conversion
+__device__ __forceinline__ float dequant(float acc, float sx, float sw, float b) {
+  const float f = sx * sw;
+  const float v = f * acc;
   return v + b;
 }
 
@@ -509,10 +548,16 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
 
 template <class C>
 __device__ __forceinline__ void zero_tail(Frags<C>& fr, int64_t kstep0, int64_t K, int lane) {
-  if (kstep0 + (lane / C::MF) * 16 >= K) {
+  constexpr int RD = C::Op::kReads;
+  const int64_t k = kstep0 + (lane / C::MF) * 16 * RD;  // K offset of the lane's first piece
 #pragma unroll
-    for (int f = 0; f < C::FM; ++f) fr.x[f] = v4i{0, 0, 0, 0};
-  }
+  for (int h = 0; h < RD; ++h)
+    if (k + 16 * h >= K) {
+#pragma unroll
+      for (int f = 0; f < C::FM; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fr.x[f][4 * h + e] = 0;
+    }
 }
 
 // Wait for the next stage's loads (this wave's) at the end of a stage.
@@ -563,7 +608,7 @@ struct Sched {
   // non-last k-step have landed: the reads issued after w[i] (rest of the
   // previous step's reads, then this step's reads so far) may stay pending
   static constexpr int row_wait(int i) {
-    const int n = (R - 1 - (C::FM + i)) + reads_before(false, i * C::FM);
+    const int n = ((R - 1 - (C::FM + i)) + reads_before(false, i * C::FM)) * C::Op::kReads;
     return n > 15 ? 15 : n;
   }
   // MFMA index after which the refill slice of row i goes out
@@ -574,9 +619,9 @@ template <class C>
 __device__ __forceinline__ void read_frag(Frags<C>& fr, int r, const int8_t* stage, uint32_t lw,
                                           uint32_t lx) {
   if (r < C::FM)
-    fr.x[r] = *reinterpret_cast<const v4i*>(stage + lx + r * C::MF * C::BK);
+    fr.x[r] = load_frag<C>(stage, lx + r * C::MF * C::BK);
   else
-    fr.w[r - C::FM] = *reinterpret_cast<const v4i*>(stage + lw + (r - C::FM) * C::MF * C::BK);
+    fr.w[r - C::FM] = load_frag<C>(stage, lw + (r - C::FM) * C::MF * C::BK);
 }
 
 template <int N>
@@ -720,7 +765,8 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
     const int fr = lane % C::MF, fq = lane / C::MF;
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
-      const uint32_t l = static_cast<uint32_t>(fr * C::BK + swz<C::kSlots>(fr, ks * (SB / 16) + fq) * 16);
+      const uint32_t l = static_cast<uint32_t>(
+          fr * C::BK + swz<C::kSlots>(fr, ks * (SB / 16) + fq * C::Op::kReads) * 16);
       lw[ks] = l + static_cast<uint32_t>(wn * C::TN * C::BK);
       lx[ks] = l + static_cast<uint32_t>(C::BN * C::BK + wm * C::TM * C::BK);
     }
@@ -1215,6 +1261,56 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
     }
   }
   return best;
+}
+
+// ------------------------------------------------------------------ FP8 --
+// Tile configurations of the e4m3 GEMM: 64-byte K steps, so BK = 128 keeps
+// two steps per stage; bf16 output only.
+namespace {
+// (A 32-byte operand doubles the fragment registers, so the wave tiles are
+// 128 x 64 / 64 x 128 / 64 x 64, not the int8 kernel's 128 x 128.)
+using F0 = Tile<256, 128, 2, 2, 128, 3, 32, true>;  // 3 x 48 KiB stages, spread refills
+using F1 = Tile<128, 256, 2, 2, 128, 3, 32, true>;  // 3 x 48 KiB stages
+using F2 = Tile<128, 128, 2, 2, 128, 4, 32, true>;  // 4 x 32 KiB stages
+const ConfigInfo kFp8Configs[] = {
+    {"fp8_bm256_bn128_bk128_s3_mf32", 256, 128, 256, 1, 1.00f},
+    {"fp8_bm128_bn256_bk128_s3_mf32", 128, 256, 256, 1, 1.00f},
+    {"fp8_bm128_bn128_bk128_s4_mf32", 128, 128, 256, 1, 0.80f},
+};
+constexpr int kNumFp8Configs = sizeof(kFp8Configs) / sizeof(kFp8Configs[0]);
+}  // namespace
+
+int gemm_fp8_num_configs() { return kNumFp8Configs; }
+
+const char* gemm_fp8_config_name(int cfg) {
+  return (cfg >= 0 && cfg < kNumFp8Configs) ? kFp8Configs[cfg].name : nullptr;
+}
+
+// Least (full-chip waves of tiles) x (tile area) / (relative throughput).
+int gemm_fp8_select_config(int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  int best = 0;
+  double best_cost = 1e300;
+  for (int c = 0; c < kNumFp8Configs; ++c) {
+    const ConfigInfo& ci = kFp8Configs[c];
+    const int64_t tiles = ((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
+    const double waves = static_cast<double>((tiles + kNumCU - 1) / kNumCU);
+    const double cost = waves * ci.BM * ci.BN / ci.rel_speed;
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm_fp8(const GemmArgs& a, int cfg, hipStream_t stream) {
+  switch (cfg) {
+    case 0: return launch_cfg<F0, false>(a, stream);
+    case 1: return launch_cfg<F1, false>(a, stream);
+    case 2: return launch_cfg<F2, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t stream) {

@@ -10,9 +10,10 @@ namespace w8a8 {
 
 // ---------------------------------------------------------- quantization --
 // Row-wise symmetric int8 quantization of bf16 (per token) or fp32 (per
-// channel) rows, optionally with GELU applied to bf16 rows first.  All sizes
+// channel) rows, optionally with GELU applied to bf16 rows first; the *Fp8
+// sources write OCP e4m3 codes (scale absmax / 448) instead.  All sizes
 // already validated by the API layer; M >= 1.
-enum class QuantSrc { kBf16, kF32, kBf16Gelu };
+enum class QuantSrc { kBf16, kF32, kBf16Gelu, kBf16Fp8, kF32Fp8 };
 
 hipError_t launch_quantize_rows(QuantSrc src, const void* x, int64_t M, int64_t K, int64_t ldx,
                                 int8_t* q, int64_t ldq, float* scale, uint16_t* h_out,
@@ -34,5 +35,12 @@ const char* gemm_config_name(int cfg);
 int gemm_select_config(int64_t M, int64_t N, int64_t K);
 // out_int32: write raw accumulators instead of the dequantized bf16.
 hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t stream);
+
+// The same GEMM on OCP e4m3 codes (qx, qw hold fp8 bytes), fp32 accumulation,
+// bf16 output with the same epilogue; its own table of tile configurations.
+int gemm_fp8_num_configs();
+const char* gemm_fp8_config_name(int cfg);
+int gemm_fp8_select_config(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_fp8(const GemmArgs& a, int cfg, hipStream_t stream);
 
 }  // namespace w8a8

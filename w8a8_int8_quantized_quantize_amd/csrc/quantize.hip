@@ -133,27 +133,58 @@ __device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2,
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
-template <int MODE>
+// FP8 (OCP e4m3) codes of four quotients: each clamped to the largest finite
+// e4m3 magnitude, 448 (so that a quotient inflated by a coarse subnormal
+// scale cannot become NaN), then converted two at a time with
+// v_cvt_pk_fp8_f32, which rounds to the nearest e4m3 value, ties to even.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// Largest code magnitude: the row's absmax maps to it.
+template <bool FP8>
+constexpr float kCodeMax = FP8 ? 448.0f : 127.0f;
+
+// Eight codes of a 16-byte chunk of bf16 values.  FP8 quotients are always
+// the IEEE division (the one-step reciprocal correction is not exact for
+// scales absmax / 448: it misses the correctly rounded quotient on about 0.2%
+// of bf16 pairs).
+template <int MODE, bool FP8 = false>
 __device__ __forceinline__ uint2 codes_bf16x8(const uint4 raw, float s, float r) {
   uint2 p;
-  p.x = pack4(code_word<MODE>(bf_lo(raw.x), s, r), code_word<MODE>(bf_hi(raw.x), s, r),
-              code_word<MODE>(bf_lo(raw.y), s, r), code_word<MODE>(bf_hi(raw.y), s, r));
-  p.y = pack4(code_word<MODE>(bf_lo(raw.z), s, r), code_word<MODE>(bf_hi(raw.z), s, r),
-              code_word<MODE>(bf_lo(raw.w), s, r), code_word<MODE>(bf_hi(raw.w), s, r));
+  if constexpr (FP8) {
+    p.x = fp8x4(bf_lo(raw.x) / s, bf_hi(raw.x) / s, bf_lo(raw.y) / s, bf_hi(raw.y) / s);
+    p.y = fp8x4(bf_lo(raw.z) / s, bf_hi(raw.z) / s, bf_lo(raw.w) / s, bf_hi(raw.w) / s);
+  } else {
+    p.x = pack4(code_word<MODE>(bf_lo(raw.x), s, r), code_word<MODE>(bf_hi(raw.x), s, r),
+                code_word<MODE>(bf_lo(raw.y), s, r), code_word<MODE>(bf_hi(raw.y), s, r));
+    p.y = pack4(code_word<MODE>(bf_lo(raw.z), s, r), code_word<MODE>(bf_hi(raw.z), s, r),
+                code_word<MODE>(bf_lo(raw.w), s, r), code_word<MODE>(bf_hi(raw.w), s, r));
+  }
   return p;
 }
 
+template <bool FP8 = false>
 __device__ __forceinline__ uint32_t codes_f32x4(const uint4 raw, float s) {
   if (s == 0.0f) return 0u;
+  if constexpr (FP8)
+    return fp8x4(__uint_as_float(raw.x) / s, __uint_as_float(raw.y) / s,
+                 __uint_as_float(raw.z) / s, __uint_as_float(raw.w) / s);
   return pack4(code_word<1>(__uint_as_float(raw.x), s, 0.f), code_word<1>(__uint_as_float(raw.y), s, 0.f),
                code_word<1>(__uint_as_float(raw.z), s, 0.f), code_word<1>(__uint_as_float(raw.w), s, 0.f));
 }
 
 // Scale of a bf16 row from its packed absmax; returns the quotient mode.
+template <bool FP8 = false>
 __device__ __forceinline__ int row_scale(u16x2 m, float& s, float& r) {
-  s = wave_max(absmax_of(m)) / 127.0f;
+  s = wave_max(absmax_of(m)) / kCodeMax<FP8>;
   if (s == 0.0f) return 0;
-  if (s >= kFastMinScale) {
+  if (!FP8 && s >= kFastMinScale) {
     r = 1.0f / s;
     return 2;
   }
@@ -161,11 +192,11 @@ __device__ __forceinline__ int row_scale(u16x2 m, float& s, float& r) {
 }
 
 // Quantize CH register-held bf16 chunks of one row (chunk j is c = lane+64j).
-template <int CH>
+template <int CH, bool FP8 = false>
 __device__ __forceinline__ void emit_bf16_row(const uint4 (&raw)[CH], int mode, float s, float r,
                                               uint32_t nch, uint32_t ln, int8_t* qrow) {
   uint2* dst = reinterpret_cast<uint2*>(qrow);
-  if (mode == 2) {
+  if (!FP8 && mode == 2) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const uint32_t c = ln + 64u * j;
@@ -175,7 +206,7 @@ __device__ __forceinline__ void emit_bf16_row(const uint4 (&raw)[CH], int mode, 
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const uint32_t c = ln + 64u * j;
-      if (c < nch) at(dst, c) = codes_bf16x8<1>(raw[j], s, r);
+      if (c < nch) at(dst, c) = codes_bf16x8<1, FP8>(raw[j], s, r);
     }
   } else {
 #pragma unroll
@@ -187,7 +218,7 @@ __device__ __forceinline__ void emit_bf16_row(const uint4 (&raw)[CH], int mode, 
 }
 
 // ------------------------------------------------------------ bf16 rows --
-template <int CH>
+template <int CH, bool FP8>
 __global__ __launch_bounds__(kThreads) void quantize_bf16_regs(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale) {
@@ -204,12 +235,13 @@ __global__ __launch_bounds__(kThreads) void quantize_bf16_regs(
     for (int j = 0; j < CH; ++j)
       m = absmax2(absmax2(absmax2(absmax2(m, raw[j].x), raw[j].y), raw[j].z), raw[j].w);
     float s, r = 0.0f;
-    const int mode = row_scale(m, s, r);
+    const int mode = row_scale<FP8>(m, s, r);
     if (lane == 0) scale[row] = s;
-    emit_bf16_row<CH>(raw, mode, s, r, nch, ln, q + row * ldq);
+    emit_bf16_row<CH, FP8>(raw, mode, s, r, nch, ln, q + row * ldq);
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) void quantize_bf16_loop(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale) {
@@ -226,13 +258,13 @@ __global__ __launch_bounds__(kThreads) void quantize_bf16_loop(
       m = absmax2(absmax2(absmax2(absmax2(m, v.x), v.y), v.z), v.w);
     }
     float s, r = 0.0f;
-    const int mode = row_scale(m, s, r);
+    const int mode = row_scale<FP8>(m, s, r);
     if (lane == 0) scale[row] = s;
     uint2* dst = reinterpret_cast<uint2*>(q + row * ldq);
     for (uint32_t c = ln; c < nch; c += 64) {
       const uint4 v = at(src, c);
-      at(dst, c) = mode == 2 ? codes_bf16x8<2>(v, s, r)
-                         : (mode == 1 ? codes_bf16x8<1>(v, s, r) : make_uint2(0u, 0u));
+      at(dst, c) = (!FP8 && mode == 2) ? codes_bf16x8<2>(v, s, r)
+                                       : (mode == 1 ? codes_bf16x8<1, FP8>(v, s, r) : make_uint2(0u, 0u));
     }
   }
 }
@@ -398,7 +430,7 @@ __device__ __forceinline__ float absmax4(float m, const uint4 v) {
   return fmaxf(m, fabsf(__uint_as_float(v.w)));
 }
 
-template <int CH>
+template <int CH, bool FP8>
 __global__ __launch_bounds__(kThreads) void quantize_f32_regs(
     const float* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale) {
@@ -413,17 +445,18 @@ __global__ __launch_bounds__(kThreads) void quantize_f32_regs(
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < CH; ++j) m = absmax4(m, raw[j]);
-    const float s = wave_max(m) / 127.0f;
+    const float s = wave_max(m) / kCodeMax<FP8>;
     if (lane == 0) scale[row] = s;
     uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * ldq);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const uint32_t c = ln + 64u * j;
-      if (c < nch) at(dst, c) = codes_f32x4(raw[j], s);
+      if (c < nch) at(dst, c) = codes_f32x4<FP8>(raw[j], s);
     }
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) void quantize_f32_loop(
     const float* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale) {
@@ -436,10 +469,10 @@ __global__ __launch_bounds__(kThreads) void quantize_f32_loop(
     const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx);
     float m = 0.0f;
     for (uint32_t c = ln; c < nch; c += 64) m = absmax4(m, at(src, c));
-    const float s = wave_max(m) / 127.0f;
+    const float s = wave_max(m) / kCodeMax<FP8>;
     if (lane == 0) scale[row] = s;
     uint32_t* dst = reinterpret_cast<uint32_t*>(q + row * ldq);
-    for (uint32_t c = ln; c < nch; c += 64) at(dst, c) = codes_f32x4(at(src, c), s);
+    for (uint32_t c = ln; c < nch; c += 64) at(dst, c) = codes_f32x4<FP8>(at(src, c), s);
   }
 }
 
@@ -448,6 +481,7 @@ __global__ __launch_bounds__(kThreads) void quantize_f32_loop(
 // no loads), take the loop kernels.
 #define W8A8_FOR_CH(X) X(1) X(2) X(3) X(4) X(6) X(8) X(12) X(16) X(24)
 
+template <bool FP8>
 hipError_t launch_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                        int64_t ldq, float* scale, hipStream_t stream) {
   const int64_t per_lane = (K / 8 + 63) / 64;
@@ -455,12 +489,12 @@ hipError_t launch_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
 #define W8A8_Q_CASE(CHV)                                                                  \
   if (K > 0 && per_lane <= CHV) {                                                                  \
-    quantize_bf16_regs<CHV><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);     \
+    quantize_bf16_regs<CHV, FP8><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale); \
     return hipGetLastError();                                                             \
   }
   W8A8_FOR_CH(W8A8_Q_CASE)
 #undef W8A8_Q_CASE
-  quantize_bf16_loop<<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
+  quantize_bf16_loop<FP8><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
   return hipGetLastError();
 }
 
@@ -480,6 +514,7 @@ hipError_t launch_gelu(const uint16_t* y, int64_t M, int64_t K, int64_t ldy, int
   return hipGetLastError();
 }
 
+template <bool FP8>
 hipError_t launch_f32(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, int64_t ldq,
                       float* scale, hipStream_t stream) {
   const int64_t per_lane = (K / 4 + 63) / 64;
@@ -487,12 +522,12 @@ hipError_t launch_f32(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t*
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
 #define W8A8_F_CASE(CHV)                                                                  \
   if (K > 0 && per_lane <= CHV) {                                                                  \
-    quantize_f32_regs<CHV><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);      \
+    quantize_f32_regs<CHV, FP8><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale); \
     return hipGetLastError();                                                             \
   }
   W8A8_FOR_CH(W8A8_F_CASE)
 #undef W8A8_F_CASE
-  quantize_f32_loop<<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
+  quantize_f32_loop<FP8><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
   return hipGetLastError();
 }
 
@@ -505,9 +540,13 @@ hipError_t launch_quantize_rows(QuantSrc src, const void* x, int64_t M, int64_t 
                                 hipStream_t stream) {
   switch (src) {
     case QuantSrc::kBf16:
-      return launch_bf16(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, stream);
+      return launch_bf16<false>(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, stream);
     case QuantSrc::kF32:
-      return launch_f32(static_cast<const float*>(x), M, K, ldx, q, ldq, scale, stream);
+      return launch_f32<false>(static_cast<const float*>(x), M, K, ldx, q, ldq, scale, stream);
+    case QuantSrc::kBf16Fp8:
+      return launch_bf16<true>(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, stream);
+    case QuantSrc::kF32Fp8:
+      return launch_f32<true>(static_cast<const float*>(x), M, K, ldx, q, ldq, scale, stream);
     case QuantSrc::kBf16Gelu:
       return launch_gelu(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, h_out,
                          stream);
