@@ -260,7 +260,19 @@ def sweep(args, torch, w8, synthetic):
                               "us_min": round(ts[0] * 1e3, 2), "TOPS": round(tops, 1),
                               "GBs": round(gbs, 1), "hbm_frac": round(gbs / 8000.0, 3),
                               "mfma_frac": round(tops / 5000.0, 3)}), flush=True)
-        del wqs
+        # the FP8 GEMM's configurations on the same shape (codes reinterpreted as e4m3)
+        wfs = [t.view(torch.uint8) & 0x77 for t in wqs]  # finite codes, |value| <= 240
+        qf = q.view(torch.uint8) & 0x77
+        for c in range(w8.w8a8_gemm_fp8_num_configs()):
+            for i in range(3):
+                w8.w8a8_gemm_dequant_fp8(qf, sx, wfs[i % ncopy], sw, b, out=y, config=c)
+            med, mn = _time_calls(torch, lambda i: w8.w8a8_gemm_dequant_fp8(qf, sx, wfs[i], sw, b, out=y, config=c),
+                                  args.sweep_iters, ncopy)
+            tops = 2.0 * s.M * s.N * s.K / (med * 1e-6) / 1e12
+            print(json.dumps({"sweep": s.name, "fp8_config": c, "name": w8.w8a8_gemm_fp8_config_name(c),
+                              "us_median": round(med, 2), "us_min": round(mn, 2), "TOPS": round(tops, 1),
+                              "mfma_frac": round(tops / 5000.0, 3)}), flush=True)
+        del wqs, wfs
 
 
 def _time_calls(torch, fn, n_iter, n_copy):
@@ -299,17 +311,22 @@ def compare(args, torch, w8, synthetic):
         w = torch.from_numpy(synthetic.weights_f32(st, s.N, s.K)).to(dev)
         b = synthetic.bias_bf16(st, s.N).to(dev)
         wq, sw = w8.w8a8_quantize_weight(w)
+        wq8, sw8 = w8.w8a8_quantize_weight_fp8(w)
         wb = w.to(torch.bfloat16)
         del w
         n8 = max(1, min(64, -(-600_000_000 // (s.N * s.K))))
         n16 = max(1, min(64, -(-600_000_000 // (2 * s.N * s.K))))
         w8s = [(wq, sw)] + [(wq.clone(), sw.clone()) for _ in range(n8 - 1)]
+        wf8 = [(wq8, sw8)] + [(wq8.clone(), sw8.clone()) for _ in range(n8 - 1)]
         wbs = [wb] + [wb.clone() for _ in range(n16 - 1)]
         y = torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty((w8.w8a8_linear_workspace_bytes(s.M, s.K),), dtype=torch.uint8, device=dev)
 
         def int8(i):
             w8.w8a8_linear(x, w8s[i][0], w8s[i][1], b, out=y, workspace=ws)
+
+        def fp8(i):
+            w8.w8a8_linear_fp8(x, wf8[i][0], wf8[i][1], b, out=y, workspace=ws)
 
         def fake(i):
             q, sx = w8.w8a8_quantize_act(x)
@@ -321,6 +338,7 @@ def compare(args, torch, w8, synthetic):
             return F.linear(x, wbs[i], b)
 
         t8 = _time_calls(torch, int8, args.sweep_iters, n8)
+        tf8 = _time_calls(torch, fp8, args.sweep_iters, n8)
         tf = _time_calls(torch, fake, args.sweep_iters, n8)
         tb = _time_calls(torch, bf16, args.sweep_iters, n16)
         int8(0)
@@ -328,13 +346,14 @@ def compare(args, torch, w8, synthetic):
         cos = F.cosine_similarity(y.float().flatten(), yf.float().flatten(), dim=0).item()
         ops = 2.0 * s.M * s.N * s.K
         print(json.dumps({"compare": s.name, "M": s.M, "K": s.K, "N": s.N,
-                          "int8_fused_us": round(t8[0], 2), "fake_int8_us": round(tf[0], 2),
+                          "int8_fused_us": round(t8[0], 2), "fp8_fused_us": round(tf8[0], 2),
+                          "fake_int8_us": round(tf[0], 2),
                           "bf16_us": round(tb[0], 2),
                           "int8_TOPS": round(ops / t8[0] / 1e6, 1), "bf16_TFLOPS": round(ops / tb[0] / 1e6, 1),
                           "speedup_vs_fake_int8": round(tf[0] / t8[0], 2),
                           "speedup_vs_bf16": round(tb[0] / t8[0], 2),
                           "cos_int8_vs_fake": round(cos, 6)}), flush=True)
-        del w8s, wbs, ws, y, x, wq, sw, wb
+        del w8s, wf8, wbs, ws, y, x, wq, sw, wq8, sw8, wb
 
 
 def main():

@@ -8,6 +8,11 @@
  * Also checks that adding 1.5 * 2^23 to the clamped quotient rounds it to the
  * same integer as rint(), with that integer's two's-complement byte in the
  * low byte of the sum's bit pattern.
+ * With the argument "448" (the FP8 kernels: s = fl32(a / 448), codes OCP
+ * e4m3) it checks instead that q' and fl32(x / s), each clamped to 448 and
+ * rounded to the e4m3 grid (round half to even, subnormal step 2^-9), give
+ * the same value.  (The quotients themselves differ in the last bit on about
+ * 0.2% of the pairs; the e4m3 codes never do.)
  * Prints "pairs N mismatches M" and exits 0 iff M == 0.  Compile with
  * -O2 -ffp-contract=off -fopenmp (fmaf must be the fused operation). */
 #include <math.h>
@@ -28,17 +33,38 @@ static uint32_t bits(float f) {
   return u;
 }
 
-int main(void) {
+/* nonnegative v clamped to 448 and rounded to the e4m3 grid, half to even */
+static double e4m3_grid(float v) {
+  double a = v > 448.0f ? 448.0 : (double)v;
+  if (a == 0.0) return 0.0;
+  int E;
+  frexp(a, &E);
+  int e = E - 1;
+  if (e < -6) e = -6;
+  const double step = ldexp(1.0, e - 3);
+  return nearbyint(a / step) * step;
+}
+
+int main(int argc, char** argv) {
   long long pairs = 0, bad = 0;
   const float min_scale = 0x1p-96f;
+  const int fp8 = argc > 1 && strcmp(argv[1], "448") == 0;
+  const float divisor = fp8 ? 448.0f : 127.0f;
 #pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, bad)
   for (int a = 1; a < 0x7F80; ++a) {
     const float amax = bf16((uint32_t)a);
-    const float s = amax / 127.0f;
+    const float s = amax / divisor;
     if (!(s >= min_scale)) continue;
     const float r = 1.0f / s;
     for (int xb = 0; xb <= a; ++xb) {
       const float x = bf16((uint32_t)xb);
+      if (fp8) {
+        const float q = x * r;
+        const float t = fmaf(fmaf(-q, s, x), r, q);
+        ++pairs;
+        if (e4m3_grid(t) != e4m3_grid(x / s)) ++bad;
+        continue;
+      }
       float want = rintf(x / s);
       want = fminf(fmaxf(want, -127.0f), 127.0f);
       const float q = x * r;

@@ -2,7 +2,8 @@
 reciprocal multiply with one fused correction step (Markstein's method) on
 rows whose scale is at least 2^-96.  This test proves, on the CPU and over
 every pair of bf16 values |x| <= absmax, that the replacement gives the same
-int8 code as the IEEE division, and that the kernels' rounding trick (adding
+int8 code as the IEEE division (scale absmax / 127), and the same e4m3 code
+for the FP8 kernels (scale absmax / 448), and that the kernels' rounding trick (adding
 1.5 * 2^23) is round-half-to-even with the code in the low byte.
 
 Host logic only: no GPU and no oracle involved."""
@@ -23,3 +24,7 @@ def test_reciprocal_quotient_matches_division_exhaustively(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     pairs = int(r.stdout.split()[1])
     assert pairs > 5 * 10 ** 8       # every (absmax, x) pair above the threshold
+    # the FP8 kernels' divisor 448: the same quotient gives the same e4m3 codes
+    r8 = subprocess.run([exe, "448"], capture_output=True, text=True, env=env, timeout=600)
+    assert r8.returncode == 0, r8.stdout + r8.stderr
+    assert int(r8.stdout.split()[1]) > 5 * 10 ** 8
