@@ -1171,8 +1171,8 @@ struct ConfigInfo {
 //             BM   BN  WM WN  BK  STAGES MFMA
 using C0 = Tile<256, 256, 2, 2, 64, 4, 32>;   // 4 waves, wave tile 128 x 128
 using C1 = Tile<256, 256, 2, 2, 128, 2, 32>;  // same, 2 deep stages
-using C2 = Tile<256, 128, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 64(n)
-using C3 = Tile<128, 256, 2, 2, 64, 4, 32>;   // wave tile 64(m) x 128(n)
+using C2 = Tile<256, 128, 2, 2, 128, 3, 32>;  // wave tile 128(m) x 64(n), 3 deep stages
+using C3 = Tile<128, 256, 2, 2, 128, 3, 32>;  // wave tile 64(m) x 128(n), 3 deep stages
 using C4 = Tile<128, 128, 2, 2, 64, 4, 32>;   // wave tile 64 x 64
 using C5 = Tile<64, 64, 2, 2, 128, 2, 32>;    // wave tile 32 x 32
 using C6 = Tile<16, 64, 1, 4, 128, 2, 16>;    // wave tile 16 x 16 (skinny M)
@@ -1181,8 +1181,8 @@ using C7 = Tile<256, 192, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 96(n)
 const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 1.00f},
     {"bm256_bn256_bk128_s2_mf32", 256, 256, 256, 1, 0.98f},
-    {"bm256_bn128_bk64_s4_mf32", 256, 128, 256, 1, 0.85f},
-    {"bm128_bn256_bk64_s4_mf32", 128, 256, 256, 1, 0.85f},
+    {"bm256_bn128_bk128_s3_mf32", 256, 128, 256, 1, 0.85f},
+    {"bm128_bn256_bk128_s3_mf32", 128, 256, 256, 1, 0.85f},
     {"bm128_bn128_bk64_s4_mf32", 128, 128, 256, 2, 0.70f},
     {"bm64_bn64_bk128_s2_mf32", 64, 64, 256, 4, 0.40f},
     {"bm16_bn64_bk128_s2_mf16", 16, 64, 256, 4, 0.15f},
