@@ -59,6 +59,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) int8_t global_i8;
 
@@ -1010,16 +1011,24 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
 //   MFMA 16x16x64 layout: lane l holds row l % 16 of a 16-row operand, K
 //   bytes 16 (l / 16) .. +15 of a 64-byte step; D[i][j] (i: weight row n,
 //   j: token m) sits in lane j + 16 (i / 4), register i % 4.
-template <int NW, int NB, bool OUT_I32, int ST, bool LOOP>
+//   FP8 operands: v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), a
+//   128-byte K step, lane l holding 32 bytes (two 16-byte loads) of row l % 16
+//   at K bytes 32 (l / 16) .. +31, fp32 accumulators, same result layout.
+template <int NW, int NB, bool OUT_I32, int ST, bool LOOP, bool FP8 = false>
 __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
-  __shared__ v4i part[NW][NB][64];
+  static_assert(!(FP8 && OUT_I32), "FP8 products accumulate in fp32: bf16 output only");
+  using Frag = std::conditional_t<FP8, v8i, v4i>;
+  using Acc = std::conditional_t<FP8, v4f, v4i>;
+  constexpr int SB = FP8 ? 128 : 64;  // K bytes of one MFMA
+  constexpr int PB = SB / 4;          // K bytes one lane supplies per step
+  __shared__ Acc part[NW][NB][64];
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int64_t M = a.M, N = a.N, K = a.K;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16 * NB;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16;
   const int r = lane % 16, kq = lane / 16;
-  const int64_t steps = (K + 63) / 64;
+  const int64_t steps = (K + SB - 1) / SB;
   const int64_t per = (steps + NW - 1) / NW;
   const int64_t s0 = wave * per, s1 = min(steps, s0 + per);
   const int64_t mr = m0 + r;
@@ -1054,22 +1063,36 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
         braw[b][e] = bsrc[n];
       }
   }
-  v4i acc[NB];
+  Acc acc[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = v4i{0, 0, 0, 0};
+  for (int b = 0; b < NB; ++b) acc[b] = Acc{};
+  // one lane's operand at K byte k of a row (kc2: its second 16-byte piece,
+  // clamped into the row when it lies past K)
+  auto load_op = [&](const int8_t* row, int64_t kc, int64_t kc2) {
+    if constexpr (FP8) {
+      const v4i lo = *reinterpret_cast<const v4i*>(row + kc);
+      const v4i hi = *reinterpret_cast<const v4i*>(row + kc2);
+      return Frag(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      (void)kc2;
+      return Frag(*reinterpret_cast<const v4i*>(row + kc));
+    }
+  };
   auto chunk = [&](int64_t c0) {
-    v4i xf[ST], wf[ST][NB];
+    Frag xf[ST], wf[ST][NB];
     // Loads only (addresses clamped into the operands): a test on loaded
     // data here would make each load wait for the one before.  Rows beyond
     // M or N only feed outputs that are never stored, so they need no
     // zeroing; steps past the wave's share are skipped below.
 #pragma unroll
     for (int i = 0; i < ST; ++i) {
-      const int64_t k = (c0 + i) * 64 + kq * 16;
-      const int64_t kc = ((c0 + i) < s1 && k < K) ? k : 0;
-      xf[i] = *reinterpret_cast<const v4i*>(xrow + kc);
+      const int64_t k = (c0 + i) * SB + kq * PB;
+      const bool in = (c0 + i) < s1 && k < K;
+      const int64_t kc = in ? k : 0;
+      const int64_t kc2 = (in && k + 16 < K) ? k + 16 : kc;
+      xf[i] = load_op(xrow, kc, kc2);
 #pragma unroll
-      for (int b = 0; b < NB; ++b) wf[i][b] = *reinterpret_cast<const v4i*>(wrow[b] + kc);
+      for (int b = 0; b < NB; ++b) wf[i][b] = load_op(wrow[b], kc, kc2);
       __builtin_amdgcn_sched_barrier(0);  // issue order = step order
     }
     // every load of the chunk is in flight before the first product
@@ -1077,11 +1100,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < ST; ++i) {
       if (c0 + i >= s1) break;  // wave-uniform
-      // the 16-byte pieces of a 64-byte step past K (K % 64 != 0) are zeroed
-      const v4i xv = ((c0 + i) * 64 + kq * 16 < K) ? xf[i] : v4i{0, 0, 0, 0};
+      // the 16-byte pieces of a step past K (K not a multiple of SB) are zeroed
+      const int64_t k = (c0 + i) * SB + kq * PB;
+      Frag xv = xf[i];
+      if (!(k < K)) xv = Frag{};
+      if constexpr (FP8) {
+        if (!(k + 16 < K)) xv = __builtin_shufflevector(xv, Frag{}, 0, 1, 2, 3, 12, 13, 14, 15);
+      }
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i][b], xv, acc[b], 0, 0, 0);
+      for (int b = 0; b < NB; ++b) {
+        if constexpr (FP8)
+          acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i][b], xv, acc[b], 0, 0, 0,
+                                                                     127, 0, 127);
+        else
+          acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i][b], xv, acc[b], 0, 0, 0);
+      }
     }
   };
   // one chunk covers the wave's share unless it exceeds ST steps; straight
@@ -1102,7 +1135,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
   const int nq = 4 * (lane / 16);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    v4i t = part[0][b][lane];
+    Acc t = part[0][b][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) t += part[w][b][lane];
     const int64_t nb = n0 + 16 * b + nq;
@@ -1110,7 +1143,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
       int32_t* out = static_cast<int32_t*>(a.out) + m * N + nb;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (nb + e < N) out[e] = t[e];
+        if (nb + e < N) out[e] = static_cast<int32_t>(t[e]);
     } else {
       uint16_t* out = static_cast<uint16_t*>(a.out) + m * N + nb;
       float v[4];
@@ -1131,11 +1164,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
   }
 }
 
-template <int NW, int NB, bool I32, int ST, bool LOOP = false>
+template <int NW, int NB, bool I32, int ST, bool LOOP = false, bool FP8 = false>
 hipError_t launch_few_rows_st(const GemmArgs& a, hipStream_t stream) {
   const int64_t gx = (a.N + 16 * NB - 1) / (16 * NB), gy = (a.M + 15) / 16;
   if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
-  gemm_few_rows<NW, NB, I32, ST, LOOP>
+  gemm_few_rows<NW, NB, I32, ST, LOOP, FP8>
       <<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), dim3(64 * NW), 0, stream>>>(a);
   return hipGetLastError();
 }
@@ -1143,17 +1176,18 @@ hipError_t launch_few_rows_st(const GemmArgs& a, hipStream_t stream) {
 // Steps in flight per wave: the smallest of 1, 2, 3, 4, 6, 8, 12 that covers
 // the wave's share of K (no load is wasted on a step past the share), else
 // a loop of 12-step chunks.
-template <int NW, int NB, bool I32>
+template <int NW, int NB, bool I32, bool FP8 = false>
 hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
-  const int64_t per = ((a.K + 63) / 64 + NW - 1) / NW;
-  if (per <= 1) return launch_few_rows_st<NW, NB, I32, 1>(a, stream);
-  if (per <= 2) return launch_few_rows_st<NW, NB, I32, 2>(a, stream);
-  if (per <= 3) return launch_few_rows_st<NW, NB, I32, 3>(a, stream);
-  if (per <= 4) return launch_few_rows_st<NW, NB, I32, 4>(a, stream);
-  if (per <= 6) return launch_few_rows_st<NW, NB, I32, 6>(a, stream);
-  if (per <= 8) return launch_few_rows_st<NW, NB, I32, 8>(a, stream);
-  if (per <= 12) return launch_few_rows_st<NW, NB, I32, 12>(a, stream);
-  return launch_few_rows_st<NW, NB, I32, 12, true>(a, stream);
+  constexpr int64_t SB = FP8 ? 128 : 64;
+  const int64_t per = ((a.K + SB - 1) / SB + NW - 1) / NW;
+  if (per <= 1) return launch_few_rows_st<NW, NB, I32, 1, false, FP8>(a, stream);
+  if (per <= 2) return launch_few_rows_st<NW, NB, I32, 2, false, FP8>(a, stream);
+  if (per <= 3) return launch_few_rows_st<NW, NB, I32, 3, false, FP8>(a, stream);
+  if (per <= 4) return launch_few_rows_st<NW, NB, I32, 4, false, FP8>(a, stream);
+  if (per <= 6) return launch_few_rows_st<NW, NB, I32, 6, false, FP8>(a, stream);
+  if (per <= 8) return launch_few_rows_st<NW, NB, I32, 8, false, FP8>(a, stream);
+  if (per <= 12) return launch_few_rows_st<NW, NB, I32, 12, false, FP8>(a, stream);
+  return launch_few_rows_st<NW, NB, I32, 12, true, FP8>(a, stream);
 }
 
 hipError_t launch_few_rows_any(const GemmArgs& a, bool i32, hipStream_t stream) {
@@ -1276,7 +1310,9 @@ const ConfigInfo kFp8Configs[] = {
     {"fp8_bm256_bn128_bk128_s3_mf32", 256, 128, 256, 1, 1.00f},
     {"fp8_bm128_bn256_bk128_s3_mf32", 128, 256, 256, 1, 1.00f},
     {"fp8_bm128_bn128_bk128_s4_mf32", 128, 128, 256, 1, 0.80f},
+    {"fp8_few_rows_splitk4_mf16", 16, 16, 256, 8, 0.10f},
 };
+constexpr int kFp8FewRows = 3;
 constexpr int kNumFp8Configs = sizeof(kFp8Configs) / sizeof(kFp8Configs[0]);
 }  // namespace
 
@@ -1286,12 +1322,15 @@ const char* gemm_fp8_config_name(int cfg) {
   return (cfg >= 0 && cfg < kNumFp8Configs) ? kFp8Configs[cfg].name : nullptr;
 }
 
-// Least (full-chip waves of tiles) x (tile area) / (relative throughput).
+// Least (full-chip waves of tiles) x (tile area) / (relative throughput); a
+// handful of tokens (M <= 16) takes the split-K few-row kernel.
 int gemm_fp8_select_config(int64_t M, int64_t N, int64_t K) {
   (void)K;
+  if (M <= 16) return kFp8FewRows;
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < kNumFp8Configs; ++c) {
+    if (c == kFp8FewRows) continue;
     const ConfigInfo& ci = kFp8Configs[c];
     const int64_t tiles = ((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
     const double waves = static_cast<double>((tiles + kNumCU - 1) / kNumCU);
@@ -1309,6 +1348,7 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 0: return launch_cfg<F0, false>(a, stream);
     case 1: return launch_cfg<F1, false>(a, stream);
     case 2: return launch_cfg<F2, false>(a, stream);
+    case 3: return launch_few_rows<4, 1, false, true>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
