@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time every GEMM configuration on every workload shape instead")
     ap.add_argument("--sweep-iters", type=int, default=20)
+    ap.add_argument("--fp8", action="store_true",
+                    help="run the step through the FP8 (e4m3) entry points instead of int8")
     ap.add_argument("--compare", action="store_true",
                     help="per workload shape: fused INT8 linear vs the 'fake INT8' path "
                          "(quantize, dequantize to bf16, bf16 GEMM) vs a plain bf16 GEMM")
@@ -157,17 +159,19 @@ def write_traffic(gf, gw, cf, cw):
     print(json.dumps(out))
 
 
-def make_inputs(torch, w8, synthetic, rotate):
+def make_inputs(torch, w8, synthetic, rotate, fp8=False):
     dev = "cuda:0"
     up, down = synthetic.CONFIGS["dit1024_mlp"]
     inp = {}
+    qw_fn = w8.w8a8_quantize_weight_fp8 if fp8 else w8.w8a8_quantize_weight
+    code = torch.uint8 if fp8 else torch.int8
 
     def lin(shape):
         st = synthetic.streams(0, shape.config_id, shape.layer_id)
         x = synthetic.activations_bf16(st, shape.M, shape.K, shape.outlier_frac).to(dev)
         w = torch.from_numpy(synthetic.weights_f32(st, shape.N, shape.K)).to(dev)
         b = synthetic.bias_bf16(st, shape.N).to(dev)
-        wq, sw = w8.w8a8_quantize_weight(w)
+        wq, sw = qw_fn(w)
         del w
         copies = [(wq, sw)] + [(wq.clone(), sw.clone()) for _ in range(rotate - 1)]
         return x, copies, b
@@ -175,10 +179,10 @@ def make_inputs(torch, w8, synthetic, rotate):
     inp["x_up"], inp["w_up"], inp["b_up"] = lin(up)
     _, inp["w_down"], inp["b_down"] = lin(down)
     M = up.M
-    inp["q_x"] = torch.empty((M, up.K), dtype=torch.int8, device=dev)
+    inp["q_x"] = torch.empty((M, up.K), dtype=code, device=dev)
     inp["s_x"] = torch.empty((M,), dtype=torch.float32, device=dev)
     inp["y_up"] = torch.empty((M, up.N), dtype=torch.bfloat16, device=dev)
-    inp["q_h"] = torch.empty((M, down.K), dtype=torch.int8, device=dev)
+    inp["q_h"] = torch.empty((M, down.K), dtype=code, device=dev)
     inp["s_h"] = torch.empty((M,), dtype=torch.float32, device=dev)
     inp["y_down"] = torch.empty((M, down.N), dtype=torch.bfloat16, device=dev)
     return up, down, inp
@@ -386,24 +390,30 @@ def main():
         compare(args, torch, w8, synthetic)
         return 0
 
-    up, down, inp = make_inputs(torch, w8, synthetic, args.rotate)
+    up, down, inp = make_inputs(torch, w8, synthetic, args.rotate, args.fp8)
     stream = torch.cuda.current_stream()
+    if args.fp8:
+        quantize, gemm, gelu_quantize = (w8.w8a8_quantize_act_fp8, w8.w8a8_gemm_dequant_fp8,
+                                         w8.w8a8_gelu_quantize_act_fp8)
+    else:
+        quantize, gemm, gelu_quantize = (w8.w8a8_quantize_act, w8.w8a8_gemm_dequant,
+                                         w8.w8a8_gelu_quantize_act)
 
     def step(i, ev=None):
         wu, su = inp["w_up"][i % len(inp["w_up"])]
         wd, sd = inp["w_down"][i % len(inp["w_down"])]
         if ev is not None:
             ev[0].record(stream)
-        w8.w8a8_quantize_act(inp["x_up"], inp["q_x"], inp["s_x"])
+        quantize(inp["x_up"], inp["q_x"], inp["s_x"])
         if ev is not None:
             ev[1].record(stream)
-        w8.w8a8_gemm_dequant(inp["q_x"], inp["s_x"], wu, su, inp["b_up"], out=inp["y_up"])
+        gemm(inp["q_x"], inp["s_x"], wu, su, inp["b_up"], out=inp["y_up"])
         if ev is not None:
             ev[2].record(stream)
-        w8.w8a8_gelu_quantize_act(inp["y_up"], inp["q_h"], inp["s_h"])
+        gelu_quantize(inp["y_up"], inp["q_h"], inp["s_h"])
         if ev is not None:
             ev[3].record(stream)
-        w8.w8a8_gemm_dequant(inp["q_h"], inp["s_h"], wd, sd, inp["b_down"], out=inp["y_down"])
+        gemm(inp["q_h"], inp["s_h"], wd, sd, inp["b_down"], out=inp["y_down"])
         if ev is not None:
             ev[4].record(stream)
 
@@ -439,7 +449,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "fp8-e4m3" if args.fp8 else "int8",
         "data": "synthetic",
         "config": {"workload": "dit1024_mlp: 4096 tokens; up-proj K=3072 N=12288; "
                                "GELU+requantize of its output; down-proj K=12288 N=3072",
@@ -459,6 +469,16 @@ def main():
             "gemm_down_config": w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(down.M, down.N, down.K)),
         },
     }
+    if args.fp8:
+        # the FP8 step: same workload on the e4m3 path (fp8 dense peak 5.0 PFLOP/s);
+        # no counters or CPU baseline for it
+        out["metric"] = METRIC + " (FP8 e4m3 variant)"
+        out["unit"] = "TFLOPS"
+        out["roofline"].update({"unit": "TFLOP/s", "traffic": None,
+                                "kernel": "gemm_kernel (FP8), up-proj M=4096 K=3072 N=12288"})
+        out["per_kernel"].pop("gemm_up_config")
+        out["per_kernel"].pop("gemm_down_config")
+        args.no_cpu_baseline = True
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(up, down, args.cpu_seconds)
     print(json.dumps(out), flush=True)

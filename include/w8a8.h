@@ -190,6 +190,11 @@ int w8a8_quantize_act_fp8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
 int w8a8_quantize_weight_fp8(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* q,
                              int64_t ldq, float* scale, void* stream);
 
+/* GELU then per-token e4m3 quantization: h as in w8a8_gelu_quantize_act, then
+ * codes and scales from h as in w8a8_quantize_act_fp8. */
+int w8a8_gelu_quantize_act_fp8(const void* y_bf16, int64_t M, int64_t K, int64_t ldy, uint8_t* q,
+                               int64_t ldq, float* scale, void* h_out_bf16, void* stream);
+
 /*
  * y[m,n] = bf16_rne((s_x[m] * s_w[n]) * acc[m,n] + bias[n]) with acc the sum
  * over k of e4m3(q_x[m,k]) * e4m3(w_q[n,k]) accumulated in fp32 on the FP8

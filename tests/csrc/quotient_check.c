@@ -59,8 +59,11 @@ int main(int argc, char** argv) {
     for (int xb = 0; xb <= a; ++xb) {
       const float x = bf16((uint32_t)xb);
       if (fp8) {
+        /* the kernels give the corrected quotient the sign of x (which also
+         * keeps x = -0 at -0, as the division does); for x >= 0 that is the
+         * identity, and the negative half mirrors this one */
         const float q = x * r;
-        const float t = fmaf(fmaf(-q, s, x), r, q);
+        const float t = copysignf(fmaf(fmaf(-q, s, x), r, q), x);
         ++pairs;
         if (e4m3_grid(t) != e4m3_grid(x / s)) ++bad;
         continue;

@@ -69,15 +69,15 @@ def test_quantize_act_fp8_bit_exact(M, K):
 def test_quantize_act_fp8_ties_and_clamp():
     # scale 1 rows (absmax 448) holding e4m3 ties, and a row whose tiny scale
     # pushes quotients past 448
-    vals = np.array([448, 1.0625, 1.1875, -1.0625, 0.0009765625, -0.0029296875, 3.25, 6.5] * 8,
-                    np.float32)
+    vals = np.array([448, 1.0625, 1.1875, -1.0625, 0.0009765625, -0.0029296875, -0.0, 6.5] * 8,
+                    np.float32)  # -0.0 keeps its sign: code 0x80
     x = np.tile(vals, (3, 1))
     x[2] = np.float32(2.0 ** -126) * np.linspace(-1, 1, x.shape[1]).astype(np.float32)
     xb = synthetic.bf16_bits(synthetic.bf16_from_f32(x))
     q, s = w8.w8a8_quantize_act_fp8(dev_bf16(xb))
     qo, so = oracle.quantize_rows_bf16_fp8(xb)
     assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
-    assert host(q)[0, :4].tolist() == [0x7E, 0x38, 0x3A, 0xB8]
+    assert host(q)[0, :4].tolist() == [0x7E, 0x38, 0x3A, 0xB8] and host(q)[0, 6] == 0x80
 
 
 @pytest.mark.parametrize("N,K", [(128, 256), (300, 1040), (64, 12288), (3, 16)])
@@ -157,3 +157,15 @@ def test_full_size_linear_fp8_sampled(shape):
     bb = synthetic.bf16_bits(b)
     qx, sx = oracle.quantize_rows_bf16_fp8(xb)
     assert_fp8_gemm_bound(bits(y)[rows], qx, sx, qw, sw, bb, shape.name)
+
+
+@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (4, 48)])
+def test_gelu_quantize_fp8_teacher_forced(M, K):
+    rng = np.random.default_rng(M + 5 * K)
+    yb = rand_bits(rng, M, K, scale=3.0, outliers=max(1, K // 100))
+    q, s, h = w8.w8a8_gelu_quantize_act_fp8(dev_bf16(yb), want_h=True)
+    assert np.array_equal(bits(h), oracle.gelu_bf16(yb))
+    qo, so = oracle.quantize_rows_bf16_fp8(bits(h))
+    assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
+    q2, s2, _ = w8.w8a8_gelu_quantize_act_fp8(dev_bf16(yb))
+    assert torch.equal(q2, q) and torch.equal(s2, s)

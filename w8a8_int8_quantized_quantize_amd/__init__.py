@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "w8a8_gemm_fp8_num_configs": ([], I),
         "w8a8_gemm_fp8_config_name": ([I], ctypes.c_char_p),
         "w8a8_linear_fp8": ([P, P, P, P, I64, I64, I64, P, P, ctypes.c_size_t, P], I),
+        "w8a8_gelu_quantize_act_fp8": ([P, I64, I64, I64, P, I64, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -332,6 +333,29 @@ def w8a8_quantize_act_fp8(x, q=None, scale=None):
 def w8a8_quantize_weight_fp8(w, q=None, scale=None):
     """Per-output-channel e4m3 quantization: fp32 [N, K] -> (uint8 codes [N, K], fp32 [N])."""
     return _quantize_rows_fp8("w8a8_quantize_weight_fp8", w, torch.float32, q, scale, "w")
+
+
+def w8a8_gelu_quantize_act_fp8(y, q=None, scale=None, h_out=None, want_h=False):
+    """GELU then per-token e4m3 quantization -> (uint8 codes, fp32 scales, h or None)."""
+    _need(y, "y", torch.bfloat16, 2)
+    M, K = y.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=y.device) if q is None else q
+    scale = torch.empty((M,), dtype=torch.float32, device=y.device) if scale is None else scale
+    if want_h and h_out is None:
+        h_out = torch.empty((M, K), dtype=torch.bfloat16, device=y.device)
+    _need(q, "q", torch.uint8, 2)
+    _need(scale, "scale", torch.float32, 1)
+    if h_out is not None:
+        _need(h_out, "h_out", torch.bfloat16, 2)
+        if tuple(h_out.shape) != (M, K) or not h_out.is_contiguous():
+            raise ValueError("h_out must be a contiguous [M, K] bf16 tensor")
+    _same_device(y, q, scale, h_out)
+    if tuple(q.shape) != (M, K) or tuple(scale.shape) != (M,) or not scale.is_contiguous():
+        raise ValueError("output shapes do not match y")
+    rc = _lib.w8a8_gelu_quantize_act_fp8(_ptr(y), M, K, _rows(y, "y"), _ptr(q), _rows(q, "q"),
+                                         _ptr(scale), _ptr(h_out), _stream(y.device))
+    _check(rc, "w8a8_gelu_quantize_act_fp8")
+    return q, scale, h_out
 
 
 def w8a8_gemm_dequant_fp8(q_x, s_x, w_q, s_w, bias=None, out=None, config=-1):

@@ -220,6 +220,17 @@ int w8a8_quantize_weight_fp8(const float* w, int64_t N, int64_t K, int64_t ldw, 
                                                nullptr, as_stream(stream)));
 }
 
+int w8a8_gelu_quantize_act_fp8(const void* y_bf16, int64_t M, int64_t K, int64_t ldy, uint8_t* q,
+                               int64_t ldq, float* scale, void* h_out_bf16, void* stream) {
+  int8_t* qb = reinterpret_cast<int8_t*>(q);
+  if (int rc = check_rows(y_bf16, M, K, ldy, 2, qb, ldq, scale)) return rc;
+  if (h_out_bf16 != nullptr && !aligned(h_out_bf16, 16)) return W8A8_ERR_ALIGN;
+  if (M == 0) return W8A8_OK;
+  return hip_status(w8a8::launch_quantize_rows(QuantSrc::kBf16GeluFp8, y_bf16, M, K, ldy, qb, ldq,
+                                               scale, static_cast<uint16_t*>(h_out_bf16),
+                                               as_stream(stream)));
+}
+
 int w8a8_gemm_dequant_fp8(const uint8_t* q_x, const float* s_x, const uint8_t* w_q,
                           const float* s_w, const void* bias_bf16, int64_t M, int64_t N, int64_t K,
                           void* y_bf16, void* stream) {

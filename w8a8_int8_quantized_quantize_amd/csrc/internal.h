@@ -13,7 +13,7 @@ namespace w8a8 {
 // channel) rows, optionally with GELU applied to bf16 rows first; the *Fp8
 // sources write OCP e4m3 codes (scale absmax / 448) instead.  All sizes
 // already validated by the API layer; M >= 1.
-enum class QuantSrc { kBf16, kF32, kBf16Gelu, kBf16Fp8, kF32Fp8 };
+enum class QuantSrc { kBf16, kF32, kBf16Gelu, kBf16Fp8, kF32Fp8, kBf16GeluFp8 };
 
 hipError_t launch_quantize_rows(QuantSrc src, const void* x, int64_t M, int64_t K, int64_t ldx,
                                 int8_t* q, int64_t ldq, float* scale, uint16_t* h_out,

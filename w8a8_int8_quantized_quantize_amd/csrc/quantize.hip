@@ -154,14 +154,16 @@ constexpr float kCodeMax = FP8 ? 448.0f : 127.0f;
 // reciprocal with one Markstein correction.  For scales absmax / 448 the
 // latter differs from the division in the last bit on about 0.2% of bf16
 // pairs, yet never in the e4m3 code it rounds to (checked over every pair of
-// bf16 values with scale >= 2^-96 on the CPU).
+// bf16 values with scale >= 2^-96 on the CPU).  The correction turns x = -0
+// into +0 (-0 + +0 rounds to +0); s > 0, so the quotient takes the sign of x,
+// which keeps e4m3's signed zero (code 0x80) as the division would.
 template <int MODE>
 __device__ __forceinline__ float quotient(float x, float s, float r) {
   if constexpr (MODE == 1) {
     return x / s;
   } else {
     const float q = x * r;
-    return __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+    return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q, s, x), r, q), x);
   }
 }
 
@@ -333,7 +335,7 @@ __device__ __forceinline__ void stage_lut(uint16_t* lut) {
 }
 
 // GELU through the staged table, absmax, optional h copy, codes.
-template <int CH>
+template <int CH, bool FP8>
 __device__ __forceinline__ void gelu_finish_row(const uint16_t* lut, uint4 (&raw)[CH], int64_t row,
                                                 int64_t K, uint32_t nch, uint32_t ln, int lane,
                                                 int8_t* q, int64_t ldq, float* scale,
@@ -359,12 +361,12 @@ __device__ __forceinline__ void gelu_finish_row(const uint16_t* lut, uint4 (&raw
     }
   }
   float s, r = 0.0f;
-  const int mode = row_scale(m, s, r);
+  const int mode = row_scale<FP8>(m, s, r);
   if (lane == 0) scale[row] = s;
-  emit_bf16_row<CH>(raw, mode, s, r, nch, ln, q + row * ldq);
+  emit_bf16_row<CH, FP8>(raw, mode, s, r, nch, ln, q + row * ldq);
 }
 
-template <int CH>
+template <int CH, bool FP8>
 __global__ __launch_bounds__(kLutThreads) void gelu_quantize_regs(
     const uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t ldy, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(kLutThreads) void gelu_quantize_regs(
     wait_vmcnt<CH>();   // loads complete in order: the older table pieces have landed
     __builtin_amdgcn_s_barrier();  // ... and so have every other wave's
     __builtin_amdgcn_sched_barrier(0);
-    gelu_finish_row<CH>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
+    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
   } else {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -392,17 +394,18 @@ __global__ __launch_bounds__(kLutThreads) void gelu_quantize_regs(
     uint4 raw[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) raw[j] = make_uint4(0u, 0u, 0u, 0u);
-    gelu_finish_row<CH>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
+    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
   }
   for (row += stride; row < M; row += stride) {
     uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
     asm volatile("" : "+v"(ln));   // from being hoisted into live registers
     uint4 raw[CH];
     load_row<CH>(reinterpret_cast<const uint4*>(y + row * ldy), nch, ln, raw);
-    gelu_finish_row<CH>(lut, raw, row, K, nch, ln, lane, q, ldq, scale, h_out);
+    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, ln, lane, q, ldq, scale, h_out);
   }
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(kLutThreads) void gelu_quantize_loop(
     const uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t ldy, int8_t* __restrict__ q,
     int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
@@ -423,15 +426,15 @@ __global__ __launch_bounds__(kLutThreads) void gelu_quantize_loop(
       m = absmax2(absmax2(absmax2(absmax2(m, v.x), v.y), v.z), v.w);
     }
     float s, r = 0.0f;
-    const int mode = row_scale(m, s, r);
+    const int mode = row_scale<FP8>(m, s, r);
     if (lane == 0) scale[row] = s;
     uint2* dst = reinterpret_cast<uint2*>(q + row * ldq);
     uint4* hrow = h_out ? reinterpret_cast<uint4*>(h_out + row * K) : nullptr;
     for (uint32_t c = ln; c < nch; c += 64) {
       const uint4 v = gelu_chunk(lut, at(src, c));
       if (hrow != nullptr) at(hrow, c) = v;
-      at(dst, c) = mode == 2 ? codes_bf16x8<2>(v, s, r)
-                         : (mode == 1 ? codes_bf16x8<1>(v, s, r) : make_uint2(0u, 0u));
+      at(dst, c) = mode == 2 ? codes_bf16x8<2, FP8>(v, s, r)
+                             : (mode == 1 ? codes_bf16x8<1, FP8>(v, s, r) : make_uint2(0u, 0u));
     }
   }
 }
@@ -512,6 +515,7 @@ hipError_t launch_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
   return hipGetLastError();
 }
 
+template <bool FP8>
 hipError_t launch_gelu(const uint16_t* y, int64_t M, int64_t K, int64_t ldy, int8_t* q,
                        int64_t ldq, float* scale, uint16_t* h_out, hipStream_t stream) {
   const int64_t per_lane = (K / 8 + 63) / 64;
@@ -519,12 +523,12 @@ hipError_t launch_gelu(const uint16_t* y, int64_t M, int64_t K, int64_t ldy, int
   const dim3 grid(static_cast<unsigned>(blocks)), block(kLutThreads);
 #define W8A8_G_CASE(CHV)                                                                     \
   if (K > 0 && per_lane <= CHV) {                                                                     \
-    gelu_quantize_regs<CHV><<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out); \
+    gelu_quantize_regs<CHV, FP8><<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out); \
     return hipGetLastError();                                                                \
   }
   W8A8_FOR_CH(W8A8_G_CASE)
 #undef W8A8_G_CASE
-  gelu_quantize_loop<<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out);
+  gelu_quantize_loop<FP8><<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out);
   return hipGetLastError();
 }
 
@@ -562,8 +566,11 @@ hipError_t launch_quantize_rows(QuantSrc src, const void* x, int64_t M, int64_t 
     case QuantSrc::kF32Fp8:
       return launch_f32<true>(static_cast<const float*>(x), M, K, ldx, q, ldq, scale, stream);
     case QuantSrc::kBf16Gelu:
-      return launch_gelu(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, h_out,
+      return launch_gelu<false>(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, h_out,
                          stream);
+    case QuantSrc::kBf16GeluFp8:
+      return launch_gelu<true>(static_cast<const uint16_t*>(x), M, K, ldx, q, ldq, scale, h_out,
+                               stream);
   }
   return hipErrorInvalidValue;
 }
