@@ -154,7 +154,12 @@ def test_module_swap_host_checks():
         w8.W8A8Linear(torch.zeros((4, 16), dtype=torch.float32), torch.ones(4))
     m = w8.W8A8Linear(torch.zeros((8, 32), dtype=torch.int8), torch.ones(8))
     assert (m.in_features, m.out_features) == (32, 8) and m.bias is None
-    assert set(m.state_dict()) == {"w_q", "s_w"}
+    assert set(m.state_dict()) == {"w_q", "s_w"} and not m.fp8
+    # uint8 codes select the FP8 (e4m3) variant
+    f = w8.W8A8Linear(torch.zeros((8, 32), dtype=torch.uint8), torch.ones(8))
+    assert f.fp8 and "e4m3" in repr(f)
+    with pytest.raises(ValueError, match="not on a GPU"):
+        w8.quantize_linears(torch.nn.Sequential(torch.nn.Linear(32, 64)), fp8=True)
     # a CPU model: layers the library takes are refused (no CPU path) ...
     cpu = torch.nn.Sequential(torch.nn.Linear(32, 64), torch.nn.GELU(), torch.nn.Linear(64, 8))
     with pytest.raises(ValueError, match="not on a GPU"):

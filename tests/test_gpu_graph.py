@@ -67,3 +67,34 @@ def test_graph_replay_matches_eager(M, N, K):
             rows = np.arange(0, M, max(1, M // 16))
             want = oracle.linear(xb[rows], host(wq), host(sw), bits(b))
             assert np.array_equal(bits(got_y)[rows], want["y"])
+
+
+def test_graph_replay_fp8_linear():
+    rng = np.random.default_rng(77)
+    M, N, K = 300, 528, 1040
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq, sw = w8.w8a8_quantize_weight_fp8(torch.from_numpy(w).to(DEV))
+    x = dev_bf16(rand_bf16_bits(rng, M, K))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty((w8.w8a8_linear_workspace_bytes(M, K),), dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        w8.w8a8_linear_fp8(x, wq, sw, out=y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w8.w8a8_linear_fp8(x, wq, sw, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        x.copy_(dev_bf16(rand_bf16_bits(rng, M, K)))
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        want = w8.w8a8_linear_fp8(x, wq, sw)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), rep
+    from test_gpu_fp8 import assert_fp8_gemm_bound
+    qx, sx = oracle.quantize_rows_bf16_fp8(bits(x))
+    assert_fp8_gemm_bound(bits(got), qx, sx, host(wq), host(sw), None, "graph fp8")

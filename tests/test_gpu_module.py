@@ -107,3 +107,26 @@ def test_include_filter_and_bias_free_layer():
         y = blk.proj(x)
     want = oracle.linear(bits(x), host(blk.proj.w_q), host(blk.proj.s_w), None)
     assert np.array_equal(bits(y), want["y"])
+
+
+def test_fp8_swapped_block_layers_within_bound():
+    from test_gpu_fp8 import assert_fp8_gemm_bound
+    ref = make_block(8)
+    blk = make_block(8)
+    assert w8.quantize_linears(blk, fp8=True) == 4
+    assert blk.up.fp8 and blk.up.w_q.dtype == torch.uint8
+    seen = {}
+    for k in ("qkv", "proj", "up", "down"):
+        getattr(blk, k).register_forward_hook(
+            lambda mod, args, out, k=k: seen.__setitem__(k, (args[0].detach().clone(), out.detach().clone())))
+    x, a = inputs(9)
+    with torch.no_grad():
+        blk(x, a)
+    for k in ("qkv", "proj", "up", "down"):
+        lin, mod = getattr(ref, k), getattr(blk, k)
+        wq, sw = oracle.quantize_rows_f32_fp8(host(lin.weight.float()))
+        assert np.array_equal(host(mod.w_q), wq) and np.array_equal(host(mod.s_w), sw), k
+        xin, yout = seen[k]
+        xb = bits(xin.reshape(-1, xin.shape[-1]))
+        qx, sx = oracle.quantize_rows_bf16_fp8(xb)
+        assert_fp8_gemm_bound(bits(yout.reshape(-1, yout.shape[-1])), qx, sx, wq, sw, bits(lin.bias), k)

@@ -432,12 +432,14 @@ class W8A8Linear(torch.nn.Module):
     swaps into the model's linears, Abstract).  The quantized weights, their
     scales and the bf16 bias are buffers, so ``state_dict()`` exports them and
     ``load_state_dict`` restores them.  Inputs must be bf16 on the GPU; leading
-    dimensions are flattened to tokens."""
+    dimensions are flattened to tokens.  With uint8 e4m3 codes for w_q (from
+    ``from_float(..., fp8=True)``) the layer runs the FP8 variant instead."""
 
     def __init__(self, w_q: torch.Tensor, s_w: torch.Tensor, bias: torch.Tensor | None = None):
         super().__init__()
-        if w_q.dtype != torch.int8 or w_q.dim() != 2:
-            raise ValueError("w_q must be an int8 [N, K] tensor")
+        if w_q.dtype not in (torch.int8, torch.uint8) or w_q.dim() != 2:
+            raise ValueError("w_q must be an int8 (or uint8 e4m3) [N, K] tensor")
+        self.fp8 = w_q.dtype == torch.uint8
         self.out_features, self.in_features = int(w_q.shape[0]), int(w_q.shape[1])
         self.register_buffer("w_q", w_q)
         self.register_buffer("s_w", s_w)
@@ -445,19 +447,21 @@ class W8A8Linear(torch.nn.Module):
         self._ws = None
 
     @classmethod
-    def from_float(cls, weight: torch.Tensor, bias: torch.Tensor | None = None) -> "W8A8Linear":
+    def from_float(cls, weight: torch.Tensor, bias: torch.Tensor | None = None,
+                   fp8: bool = False) -> "W8A8Linear":
         """Quantize a float weight [N, K] (and take a bias) already on the GPU."""
-        w_q, s_w = w8a8_quantize_weight(weight.detach().float().contiguous())
+        quant = w8a8_quantize_weight_fp8 if fp8 else w8a8_quantize_weight
+        w_q, s_w = quant(weight.detach().float().contiguous())
         b = bias.detach().to(torch.bfloat16).contiguous() if bias is not None else None
         return cls(w_q, s_w, b)
 
     @classmethod
-    def from_linear(cls, linear: torch.nn.Linear) -> "W8A8Linear":
-        return cls.from_float(linear.weight, linear.bias)
+    def from_linear(cls, linear: torch.nn.Linear, fp8: bool = False) -> "W8A8Linear":
+        return cls.from_float(linear.weight, linear.bias, fp8)
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"bias={self.bias is not None}")
+                f"bias={self.bias is not None}, codes={'e4m3' if self.fp8 else 'int8'}")
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
@@ -465,16 +469,17 @@ class W8A8Linear(torch.nn.Module):
         need = w8a8_linear_workspace_bytes(x2.shape[0], x2.shape[1])
         if self._ws is None or self._ws.numel() < need or self._ws.device != x2.device:
             self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
-        y = w8a8_linear(x2, self.w_q, self.s_w, self.bias, workspace=self._ws)
+        fn = w8a8_linear_fp8 if self.fp8 else w8a8_linear
+        y = fn(x2, self.w_q, self.s_w, self.bias, workspace=self._ws)
         return y.reshape(*lead, self.out_features)
 
 
-def quantize_linears(module: torch.nn.Module, include=None) -> int:
+def quantize_linears(module: torch.nn.Module, include=None, fp8: bool = False) -> int:
     """Replace, in place, every ``nn.Linear`` inside ``module`` whose input
     width the library takes (a multiple of 16, at most W8A8_MAX_K) by a
-    W8A8Linear quantized from its weights; ``include(name, linear)`` may
-    narrow the choice.  The linears must already be on the GPU.  Returns the
-    number of layers replaced."""
+    W8A8Linear quantized from its weights (e4m3 codes with ``fp8``);
+    ``include(name, linear)`` may narrow the choice.  The linears must already
+    be on the GPU.  Returns the number of layers replaced."""
     count = 0
     for name, child in list(module.named_children()):
         if isinstance(child, torch.nn.Linear):
@@ -483,8 +488,8 @@ def quantize_linears(module: torch.nn.Module, include=None) -> int:
                 if child.weight.device.type != "cuda":
                     raise ValueError(f"quantize_linears: layer {name!r} is not on a GPU "
                                      f"(weights are quantized by the library's GPU kernel)")
-                setattr(module, name, W8A8Linear.from_linear(child))
+                setattr(module, name, W8A8Linear.from_linear(child, fp8))
                 count += 1
         else:
-            count += quantize_linears(child, include)
+            count += quantize_linears(child, include, fp8)
     return count
