@@ -6,12 +6,16 @@
 // epilogue folds the two scales and the bias, autotuned per GEMM shape.  The
 // paper's kernel targets Ampere tensor cores; this one is designed for CDNA4:
 //
-//  * MFMA v_mfma_i32_32x32x32_i8 (v_mfma_i32_16x16x64_i8 for the 16-row
-//    tiles).  The weight tile is the MFMA "A" operand and the activation tile
-//    the "B" operand, so a result block holds D[n][m]: each lane owns runs of
-//    four consecutive output columns n of one row m; lanes l and l + 32 hold
-//    the two halves of eight consecutive columns, which the epilogue joins
-//    (v_permlane32_swap) into one 16-byte bf16 store per lane.
+//  * MFMA v_mfma_i32_32x32x32_i8 or v_mfma_i32_16x16x64_i8.  The weight tile
+//    is the MFMA "A" operand and the activation tile the "B" operand, so a
+//    result block holds D[n][m]: each lane owns runs of four consecutive
+//    output columns n of one row m; the epilogue joins two such runs held by
+//    different lanes (v_permlane32_swap for 32x32 blocks, v_permlane16_swap
+//    across two 16x16 blocks) into one 16-byte bf16 store per lane.  The
+//    16x16x64 form moves half the accumulator bytes per operation of the
+//    32x32x32 one and draws less power per operation; under the chip's power
+//    limit its 256 x 256 tile runs at a higher clock and is the faster one on
+//    the large shapes.
 //  * Both operands are K-contiguous ([M,K] and [N,K] row-major), which is what
 //    the MFMA operand layout wants: every lane reads 16 consecutive k of one
 //    row with a single ds_read_b128, no transposes anywhere.
@@ -83,7 +87,9 @@ __device__ __forceinline__ int swz(int r, int c) {
 // result D[i][j] sits in lane j + 32 ((i / 4) % 2), register (i % 4) + 4 (i / 8).
 // MF = 16: v_mfma_i32_16x16x64_i8, 64 bytes of K per step; lane l holds row
 // l % 16, K bytes 16 (l / 16) .. +15, and D[i][j] sits in lane j + 16 (i / 4),
-// register i % 4.
+// register i % 4.  (Which K bytes of a step feed which of these positions is
+// set by piece_chunk below: any assignment shared by both operands gives the
+// same sums.)
 template <int MF, bool FP8 = false>
 struct Mfma;
 // kStepBytes: K bytes of one MFMA; Frag: one lane's operand, read from LDS
@@ -120,6 +126,25 @@ struct Mfma<32, true> {
   }
 };
 
+// Which 16-byte chunk of a k-step piece h of a lane holds, for lane group
+// q = lane / MF.  The K positions inside one MFMA are summed in any order, so
+// the lane -> chunk assignment is free as long as both operands use the same
+// one.  It is chosen for the LDS: the reads of lanes l and l + 32 are served
+// together, and they must fall in different banks.  With the natural order
+// they read chunks two apart for the 16x16x64 operands (q = 0 / 2) and for the
+// first pieces of the FP8 32-byte operands, which the swizzle maps to the
+// same banks (measured: SQ_LDS_BANK_CONFLICT 4 cycles per fragment read).
+// Adjacent chunks, as the 32x32x32 int8 operands read them, never conflict:
+//   int8 32x32x32: q                       (lanes l, l + 32: chunks c, c + 1)
+//   int8 16x16x64: q = 0, 1, 2, 3 -> 0, 2, 1, 3
+//   FP8 32x32x64:  pieces q and q + 2      (lanes l, l + 32: c, c + 1 and c + 2, c + 3)
+template <int MF, bool FP8>
+__device__ __forceinline__ int piece_chunk(int q, int h) {
+  if constexpr (FP8) return q + 2 * h;
+  else if constexpr (MF == 16) return ((q & 1) << 1) | (q >> 1);
+  else return q;
+}
+
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, int MF_, bool FP8_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
@@ -141,7 +166,7 @@ struct Tile {
   // buffer they refill (one slice per MFMA row)
   static constexpr bool kSpread = STAGES >= 3;
   static_assert(BK == 64 || BK == 128, "BK");
-  static_assert(kSteps >= 2 && kSteps % 2 == 0, "fragment sets alternate within a stage");
+  static_assert(kSteps == 1 || kSteps % 2 == 0, "fragment sets alternate per k-step");
   static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be whole MFMA blocks");
   static_assert(BN % 16 == 0 && BM % 16 == 0 && BM % kRowsPerLoad == 0, "load blocks");
   static_assert((BN / kRowsPerLoad) % kWaves == 0 || kLoads <= kWaves,
@@ -152,11 +177,13 @@ struct Tile {
   static_assert(STAGES >= 2 && STAGES * kStage <= 160 * 1024, "LDS budget");
 };
 
-// Store instructions one wave of the interior-tile bf16 epilogue issues
-// (one per pair of 4-column groups when the groups pair up).
+// Store instructions one wave of the interior-tile bf16 epilogue issues: one
+// 16-byte store per pair of 4-column groups (32x32 blocks: the block's own
+// groups pair up; 16x16 blocks: two blocks of adjacent rows pair up).
 template <class C>
-constexpr int kFastStores =
-    C::Op::kGroups % 2 == 0 ? C::FM * C::FN * C::Op::kGroups / 2 : C::FM * C::FN * C::Op::kGroups;
+constexpr int kFastStores = (C::Op::kGroups % 2 == 0 || (C::MF == 16 && C::FM % 2 == 0))
+                                ? C::FM * C::FN * C::Op::kGroups / 2
+                                : C::FM * C::FN * C::Op::kGroups;
 
 // Map a linear tile index to (tile_m, tile_n): XCD-contiguous ranges, then
 // grouped order inside a range.
@@ -319,16 +346,16 @@ struct Frags {
 };
 
 // One lane's operand at byte offset `off` of an LDS stage.  A two-piece
-// (32-byte) operand is the logical 16-byte chunks 2c and 2c + 1 of its row;
-// the chunk swizzle is an XOR on the chunk index, so their slots differ only
-// in the lowest bit: offsets off and off ^ 16.
+// (32-byte) operand is the logical 16-byte chunks c and c + 2 of its row (c
+// even modulo 4, see piece_chunk); the chunk swizzle is an XOR on the chunk
+// index, so their slots differ only in bit 1: offsets off and off ^ 32.
 template <class C>
 __device__ __forceinline__ typename C::Op::Frag load_frag(const int8_t* stage, uint32_t off) {
   if constexpr (C::Op::kReads == 1) {
     return *reinterpret_cast<const v4i*>(stage + off);
   } else {
     const v4i lo = *reinterpret_cast<const v4i*>(stage + off);
-    const v4i hi = *reinterpret_cast<const v4i*>(stage + (off ^ 16u));
+    const v4i hi = *reinterpret_cast<const v4i*>(stage + (off ^ 32u));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
@@ -500,6 +527,40 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
       bb[fi][g] = bp ? *reinterpret_cast<const uint2*>(bp + n) : nobias;
     }
   uint16_t* y = static_cast<uint16_t*>(a.out);
+  // group g of block (fi, fj), dequantized and packed to 4 bf16
+  auto pack = [&](int fi, int fj, int g) {
+    const typename C::Acc& d = acc[fi][fj];
+    const float swv[4] = {sw[fi][g].x, sw[fi][g].y, sw[fi][g].z, sw[fi][g].w};
+    const float bv[4] = {__uint_as_float(bb[fi][g].x << 16), __uint_as_float(bb[fi][g].x & 0xFFFF0000u),
+                         __uint_as_float(bb[fi][g].y << 16), __uint_as_float(bb[fi][g].y & 0xFFFF0000u)};
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = dequant(d[4 * g + e], sx[fj], swv[e], bv[e]);
+    return make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
+  };
+  if constexpr (MF == 16 && C::FM % 2 == 0) {
+    // 16x16 blocks: lane l holds columns 4 (l / 16) .. +3 of row l % 16.
+    // v_permlane16_swap exchanges the odd 16-lane rows of its first operand
+    // with the even rows of its second; applied to blocks fj and fj + 1 (the
+    // next 16 output rows), every lane then holds 8 consecutive columns of
+    // one row: lane row r = l / 16 stores row (fj + (r & 1)) 16 + l % 16,
+    // columns 8 (r >> 1) .. +7 of the block, in one 16-byte store.
+#pragma unroll
+    for (int fj = 0; fj < C::FM; fj += 2) {
+#pragma unroll
+      for (int fi = 0; fi < C::FN; ++fi) {
+        __builtin_amdgcn_sched_barrier(0);
+        const uint2 pa = pack(fi, fj, 0), pb = pack(fi, fj + 1, 0);
+        const auto sx2 = __builtin_amdgcn_permlane16_swap(pa.x, pb.x, false, false);
+        const auto sy2 = __builtin_amdgcn_permlane16_swap(pa.y, pb.y, false, false);
+        const uint4 o = make_uint4(sx2[0], sy2[0], sx2[1], sy2[1]);
+        const int64_t m = m0 + wm * C::TM + (fj + (lq & 1)) * MF + lr;
+        const int64_t n = n0 + wn * C::TN + fi * MF + (lq >> 1) * 8;
+        *reinterpret_cast<uint4*>(y + m * a.N + n) = o;
+      }
+    }
+    return;
+  }
   // row blocks outermost: the 16 stores of one row block complete its
   // output rows' 256-byte runs back to back, so L2 merges whole lines
   // before it writes them back (interleaving row blocks left half-written
@@ -510,19 +571,9 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
     for (int fi = 0; fi < C::FN; ++fi) {
       __builtin_amdgcn_sched_barrier(0);
       const int64_t m = m0 + wm * C::TM + fj * MF + lr;
-      const typename C::Acc d = acc[fi][fj];
       uint2 pk[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float swv[4] = {sw[fi][g].x, sw[fi][g].y, sw[fi][g].z, sw[fi][g].w};
-        const float bv[4] = {__uint_as_float(bb[fi][g].x << 16), __uint_as_float(bb[fi][g].x & 0xFFFF0000u),
-                             __uint_as_float(bb[fi][g].y << 16), __uint_as_float(bb[fi][g].y & 0xFFFF0000u)};
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = dequant(d[4 * g + e], sx[fj], swv[e], bv[e]);
-        pk[g].x = bf16_pair(v[0], v[1]);
-        pk[g].y = bf16_pair(v[2], v[3]);
-      }
+      for (int g = 0; g < G; ++g) pk[g] = pack(fi, fj, g);
       const int64_t nb = n0 + wn * C::TN + fi * MF;
       if constexpr (G % 2 == 0) {
         // Lanes l and l + 32 hold the two 4-column halves of each 8-column
@@ -550,10 +601,10 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
 template <class C>
 __device__ __forceinline__ void zero_tail(Frags<C>& fr, int64_t kstep0, int64_t K, int lane) {
   constexpr int RD = C::Op::kReads;
-  const int64_t k = kstep0 + (lane / C::MF) * 16 * RD;  // K offset of the lane's first piece
+  const int q = lane / C::MF;
 #pragma unroll
   for (int h = 0; h < RD; ++h)
-    if (k + 16 * h >= K) {
+    if (kstep0 + 16 * piece_chunk<C::MF, C::kFp8>(q, h) >= K) {  // piece h lies past K
 #pragma unroll
       for (int f = 0; f < C::FM; ++f)
 #pragma unroll
@@ -684,15 +735,20 @@ __device__ __forceinline__ void step_mfmas(const Loader<C, FAST>& ld, const Frag
 // also means every wave's reads of this stage are done, freeing its buffer
 // for a refill; and it reads the next stage's first fragments.  Without
 // OPEN (a tile's last stage) it only waits for its own fragments.
-template <class C, bool FAST, bool OPEN, bool EXT, int KS, int KSEND, bool XST = false>
+// PAR: which of the two fragment sets k-step 0 of this stage uses.  A stage
+// of an even number of k-steps starts and ends on set 0.  With one k-step per
+// stage the steady-state loop alternates the sets (PAR 0, then 1); every other
+// stage runs with PAR 0 and then moves the next stage's fragments into set 0
+// (next_to_current), so a stage always begins with its fragments in set 0.
+template <class C, bool FAST, bool OPEN, bool EXT, int KS, int KSEND, bool XST = false, int PAR = 0>
 __device__ __forceinline__ void stage_steps(const Loader<C, FAST>& ld, Frags<C> (&f)[2],
                                             typename C::Acc (&acc)[C::FN][C::FM], const int8_t* cur,
                                             const int8_t* next, const uint32_t* lw,
                                             const uint32_t* lx, const Refill& rf, int ahead,
                                             int wave, int lane) {
   if constexpr (KS < KSEND) {
-    Frags<C>& fc = f[KS & 1];
-    Frags<C>& fn = f[(KS + 1) & 1];
+    Frags<C>& fc = f[(KS + PAR) & 1];
+    Frags<C>& fn = f[(KS + 1 + PAR) & 1];
     sched_fence();
     if constexpr (KS + 1 < C::kSteps) {
       step_mfmas<C, FAST, true, EXT, KS, 0>(ld, fc, fn, acc, cur, lw[KS + 1], lx[KS + 1], rf, wave,
@@ -705,10 +761,11 @@ __device__ __forceinline__ void stage_steps(const Loader<C, FAST>& ld, Frags<C> 
       wait_lds();
       step_mfmas<C, FAST, false, EXT, KS, 0>(ld, fc, fn, acc, next, lw[0], lx[0], rf, wave, lane);
     }
-    stage_steps<C, FAST, OPEN, EXT, KS + 1, KSEND, XST>(ld, f, acc, cur, next, lw, lx, rf, ahead,
-                                                        wave, lane);
+    stage_steps<C, FAST, OPEN, EXT, KS + 1, KSEND, XST, PAR>(ld, f, acc, cur, next, lw, lx, rf, ahead,
+                                                             wave, lane);
   }
 }
+
 
 // Stages the prologue of a tile loads before its K loop.  Every wave issues
 // the same load sequence whatever KST is: the prologue stages and each
@@ -760,14 +817,14 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
   Loader<C, FAST> ld(a, n0, m0, wave, lane);
   auto buf = [&](int st) { return smem + ((ph + st) % S) * C::kStage; };
 
-  // fragment addressing: row (MF f + lane % MF), chunk (step SB/16 + lane / MF)
+  // fragment addressing: row (MF f + lane % MF), chunk (step SB/16 + piece_chunk(lane / MF, 0))
   uint32_t lw[NS], lx[NS];
   {
     const int fr = lane % C::MF, fq = lane / C::MF;
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
       const uint32_t l = static_cast<uint32_t>(
-          fr * C::BK + swz<C::kSlots>(fr, ks * (SB / 16) + fq * C::Op::kReads) * 16);
+          fr * C::BK + swz<C::kSlots>(fr, ks * (SB / 16) + piece_chunk<C::MF, C::kFp8>(fq, 0)) * 16);
       lw[ks] = l + static_cast<uint32_t>(wn * C::TN * C::BK);
       lx[ks] = l + static_cast<uint32_t>(C::BN * C::BK + wm * C::TM * C::BK);
     }
@@ -782,10 +839,14 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
     // stage 0 landed; with `stored`, the previous tile's epilogue issued
     // kFastStores stores after this tile's first PRO stages, which need not
     // have completed
-    if (stored && C::kSpread)
-      wait_vm<(PRO - 1) * C::kLoadsPerWave + kFastStores<C>>();
-    else
+    if constexpr (C::kSpread) {
+      if (stored)
+        wait_vm<(PRO - 1) * C::kLoadsPerWave + kFastStores<C>>();
+      else
+        wait_stages<C>(PRO - 1);
+    } else {
       wait_stages<C>(PRO - 1);
+    }
     block_barrier();
     Frags<C> f[2];
     read_frags<C>(f[0], buf(0), lw[0], lx[0]);
@@ -816,14 +877,21 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
       return r;
     };
     auto head = [&](auto ext, int st) {
-      const Refill r = refill_of(st);
-      stage_steps<C, FAST, true, decltype(ext)::value, 0, NS - 1>(ld, f, acc, buf(st), buf(st + 1), lw,
-                                                                 lx, r, S - 2, wave, lane);
+      if constexpr (NS > 1) {
+        const Refill r = refill_of(st);
+        stage_steps<C, FAST, true, decltype(ext)::value, 0, NS - 1>(ld, f, acc, buf(st), buf(st + 1),
+                                                                   lw, lx, r, S - 2, wave, lane);
+      }
+    };
+    // one k-step per stage: the next stage's fragments were read into set 1
+    auto next_to_current = [&]() {
+      if constexpr (NS == 1) f[0] = f[1];
     };
     auto tail = [&](auto ext, int st) {
       const Refill r = refill_of(st);
       stage_steps<C, FAST, true, decltype(ext)::value, NS - 1, NS>(ld, f, acc, buf(st), buf(st + 1),
                                                                   lw, lx, r, S - 2, wave, lane);
+      next_to_current();
     };
     // a tail whose wait also lets the previous epilogue's stores stay in
     // flight (the next stage was loaded before them)
@@ -831,6 +899,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
       const Refill r = refill_of(st);
       stage_steps<C, FAST, true, false, NS - 1, NS, true>(ld, f, acc, buf(st), buf(st + 1), lw, lx, r,
                                                           S - 2, wave, lane);
+      next_to_current();
     };
     using Own = std::false_type;
     using Ext = std::true_type;
@@ -847,6 +916,19 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
         for (; st < S - 2; ++st) {
           tail_xst(st);
           head(Own{}, st + 1);
+        }
+      }
+      if constexpr (NS == 1) {
+        // one k-step per stage: the fragment sets alternate with the stage,
+        // so the steady-state loop runs two stages per iteration with
+        // compile-time sets (st is even here)
+        for (; st + 2 < own_end; st += 2) {
+          const Refill r0 = refill_of(st);
+          stage_steps<C, FAST, true, false, 0, 1, false, 0>(ld, f, acc, buf(st), buf(st + 1), lw, lx,
+                                                            r0, S - 2, wave, lane);
+          const Refill r1 = refill_of(st + 1);
+          stage_steps<C, FAST, true, false, 0, 1, false, 1>(ld, f, acc, buf(st + 1), buf(st + 2), lw,
+                                                            lx, r1, S - 2, wave, lane);
         }
       }
       for (; st + 1 < own_end; ++st) {
@@ -881,6 +963,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
         tail(Own{}, nfull - 1);
       }
       {
+        constexpr int P = 0;
         const int st = KST - 1;
         const int8_t* cur = buf(st);
         const int64_t k0 = static_cast<int64_t>(st) * C::BK;
@@ -891,10 +974,10 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
           sched_fence();
           wait_lds();
           if (ks + 1 < NS && (FAST || ksk + SB < a.K))
-            read_frags<C>(f[(ks + 1) & 1], cur, lw[ks + 1], lx[ks + 1]);
-          if (!FAST && ksk + SB > a.K) zero_tail<C>(f[ks & 1], ksk, a.K, lane);
+            read_frags<C>(f[(ks + 1 + P) & 1], cur, lw[ks + 1], lx[ks + 1]);
+          if (!FAST && ksk + SB > a.K) zero_tail<C>(f[(ks + P) & 1], ksk, a.K, lane);
           sched_fence();
-          mfma_step<C>(f[ks & 1], acc);
+          mfma_step<C>(f[(ks + P) & 1], acc);
         }
       }
       // the repeated loads past the last stage must land before the buffers
@@ -1211,9 +1294,10 @@ using C4 = Tile<128, 128, 2, 2, 64, 4, 32>;   // wave tile 64 x 64
 using C5 = Tile<64, 64, 2, 2, 128, 2, 32>;    // wave tile 32 x 32
 using C6 = Tile<16, 64, 1, 4, 128, 2, 16>;    // wave tile 16 x 16 (skinny M)
 using C7 = Tile<256, 192, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 96(n)
+using C9 = Tile<256, 256, 2, 2, 64, 4, 16>;   // C0 on 16x16x64 blocks, one k-step per stage
 
 const ConfigInfo kConfigs[] = {
-    {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 1.00f},
+    {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 0.97f},
     {"bm256_bn256_bk128_s2_mf32", 256, 256, 256, 1, 0.98f},
     {"bm256_bn128_bk128_s3_mf32", 256, 128, 256, 1, 0.85f},
     {"bm128_bn256_bk128_s3_mf32", 128, 256, 256, 1, 0.85f},
@@ -1222,6 +1306,7 @@ const ConfigInfo kConfigs[] = {
     {"bm16_bn64_bk128_s2_mf16", 16, 64, 256, 4, 0.15f},
     {"bm256_bn192_bk64_s4_mf32", 256, 192, 256, 1, 0.92f},
     {"few_rows_splitk4_mf16", 16, 16, 256, 8, 0.10f},
+    {"bm256_bn256_bk64_s4_mf16", 256, 256, 256, 1, 1.00f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kSkinny = 6;    // 16-row tiled kernel
@@ -1365,6 +1450,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 6: return launch_cfg_out<C6>(a, out_int32, stream);
     case 7: return launch_cfg_out<C7>(a, out_int32, stream);
     case 8: return launch_few_rows_any(a, out_int32, stream);
+    case 9: return launch_cfg_out<C9>(a, out_int32, stream);
     default: return hipErrorInvalidValue;
   }
 }
