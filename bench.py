@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--compare", action="store_true",
                     help="per workload shape: fused INT8 linear vs the 'fake INT8' path "
                          "(quantize, dequantize to bf16, bf16 GEMM) vs a plain bf16 GEMM")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="matrix-core rate on the up-proj's own int8 / e4m3 codes with no memory "
+                         "traffic (the power-limited ceiling), next to the GEMM on the same codes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of known size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -371,6 +374,88 @@ def compare(args, torch, w8, synthetic):
         del w8s, wf8, wbs, ws, y, x, wq, sw, wq8, sw8, wb
 
 
+def mfma_ceiling(args, torch, w8, synthetic):
+    """Matrix-core throughput on the up-proj's own codes with nothing else
+    running (csrc/mfma_ceiling.hip, built into libw8a8_probe.so), and the clock
+    it runs at, next to the up-proj GEMM on the same codes.  Each probe launch
+    does the up-proj GEMM's share of work per CU (4 waves x 144 iterations x
+    2^22 operations = 1.21 GOP per CU); the codes are the first bytes of the
+    GEMM's weight codes (MFMA "A") and per-token activation codes ("B")."""
+    import ctypes
+
+    dev = "cuda:0"
+    lib = ctypes.CDLL(os.path.join(ROOT, "w8a8_int8_quantized_quantize_amd", "libw8a8_probe.so"))
+    P = ctypes.c_void_p
+    lib.w8a8_probe_mfma_ceiling.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int,
+                                            ctypes.c_int, P, P, P]
+    lib.w8a8_probe_mfma_ceiling.restype = ctypes.c_int
+    lib.w8a8_probe_mfma_ops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.w8a8_probe_mfma_ops.restype = ctypes.c_double
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 144
+    need = grid * 256 * 8 * 16
+    s = synthetic.CONFIGS["dit1024_mlp"][0]
+    st = synthetic.streams(0, s.config_id, s.layer_id)
+    x = synthetic.activations_bf16(st, s.M, s.K, s.outlier_frac).to(dev)
+    w = torch.from_numpy(synthetic.weights_f32(st, s.N, s.K)).to(dev)
+    b = synthetic.bias_bf16(st, s.N).to(dev)
+    q, sx = w8.w8a8_quantize_act(x)
+    wq, sw = w8.w8a8_quantize_weight(w)
+    qf, sxf = w8.w8a8_quantize_act_fp8(x)
+    wqf, swf = w8.w8a8_quantize_weight_fp8(w)
+    del w
+    flat = lambda t: t.view(torch.uint8).reshape(-1)[:need].contiguous()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    uni = lambda: torch.randint(-127, 128, (need,), dtype=torch.int8, device=dev, generator=gen).view(torch.uint8)
+    zero = torch.zeros(need, dtype=torch.uint8, device=dev)
+    cases = [
+        ("int8 32x32x32, workload codes", 0, flat(wq), flat(q)),
+        ("int8 16x16x64, workload codes", 1, flat(wq), flat(q)),
+        ("int8 32x32x32 + LDS fragment reads, workload codes", 2, flat(wq), flat(q)),
+        ("int8 16x16x64 + LDS fragment reads, workload codes", 4, flat(wq), flat(q)),
+        ("fp8 e4m3 32x32x64, workload codes", 3, flat(wqf), flat(qf)),
+        ("int8 32x32x32, uniform random codes", 0, uni(), uni()),
+        ("int8 16x16x64, uniform random codes", 1, uni(), uni()),
+        ("int8 32x32x32, all zero", 0, zero, zero),
+        ("int8 16x16x64, all zero", 1, zero, zero),
+    ]
+    sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    stamps = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ops = lib.w8a8_probe_mfma_ops(grid, iters)
+    res = {}
+    for name, mode, a, bb in cases:
+        def launch(_i=0):
+            rc = lib.w8a8_probe_mfma_ceiling(mode, a.data_ptr(), bb.data_ptr(), need, grid, iters,
+                                             sink.data_ptr(), stamps.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"w8a8_probe_mfma_ceiling returned {rc}")
+        for _ in range(10):
+            launch()
+        med, mn = _time_calls(torch, launch, 30, 1)
+        t = stamps.view(grid, 2).cpu().double()
+        ghz = float((t[:, 0] / (t[:, 1] * 10.0)).mean())
+        tops = ops / (med * 1e-6) / 1e12
+        res[name] = tops
+        print(json.dumps({"mfma_ceiling": name, "us_median": round(med, 2), "TOPS": round(tops, 1),
+                          "frac_of_spec": round(tops / PEAK_INT8_TOPS, 3), "clock_GHz": round(ghz, 3),
+                          "issue_frac_at_clock": round(tops * 1e12 / (grid * 8192 * ghz * 1e9), 3)}),
+              flush=True)
+    # the GEMM itself on the same codes, weights rotated past the last-level cache
+    ncopy = max(1, min(64, -(-600_000_000 // (s.N * s.K))))
+    wqs = [wq] + [wq.clone() for _ in range(ncopy - 1)]
+    y = torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)
+    med, mn = _time_calls(torch, lambda i: w8.w8a8_gemm_dequant(q, sx, wqs[i], sw, b, out=y),
+                          args.sweep_iters, ncopy)
+    tops = 2.0 * s.M * s.N * s.K / (med * 1e-6) / 1e12
+    cfg = w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(s.M, s.N, s.K))
+    print(json.dumps({"gemm": s.name, "config": cfg, "us_median": round(med, 2), "TOPS": round(tops, 1),
+                      "frac_of_spec": round(tops / PEAK_INT8_TOPS, 3),
+                      "frac_of_ceiling": {k: round(tops / v, 3) for k, v in res.items()
+                                          if "workload" in k and "fp8" not in k}}), flush=True)
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -399,6 +484,9 @@ def main():
         return 0
     if args.compare:
         compare(args, torch, w8, synthetic)
+        return 0
+    if args.mfma_ceiling:
+        mfma_ceiling(args, torch, w8, synthetic)
         return 0
 
     up, down, inp = make_inputs(torch, w8, synthetic, args.rotate, args.fp8)
