@@ -379,7 +379,7 @@ def mfma_ceiling(args, torch, w8, synthetic):
     running (csrc/mfma_ceiling.hip, built into libw8a8_probe.so), and the clock
     it runs at, next to the up-proj GEMM on the same codes.  Each probe launch
     does the up-proj GEMM's share of work per CU (4 waves x 144 iterations x
-    2^22 operations = 1.21 GOP per CU); the codes are the first bytes of the
+    2^21 operations = 1.21 GOP per CU); the codes are the first bytes of the
     GEMM's weight codes (MFMA "A") and per-token activation codes ("B")."""
     import ctypes
 

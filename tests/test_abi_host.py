@@ -183,8 +183,8 @@ def test_probe_library_host_checks():
     f = pl.w8a8_probe_mfma_ceiling
     f.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, P]
     f.restype = ctypes.c_int
-    # 256 workgroups x 4 waves x 144 iterations x 2^22 operations
-    assert pl.w8a8_probe_mfma_ops(256, 144) == 256 * 4 * 144 * 2.0 ** 22
+    # 256 workgroups x 4 waves x 144 iterations x 2^21 operations
+    assert pl.w8a8_probe_mfma_ops(256, 144) == 256 * 4 * 144 * 2.0 ** 21
     need = 256 * 256 * 8 * 16
     assert f(0, None, A, need, 256, 144, A, A, None) == -1           # null operand
     assert f(5, A, A, need, 256, 144, A, A, None) == -1              # unknown mode

@@ -195,7 +195,8 @@ __global__ __launch_bounds__(kThreads) void mfma_ceiling(const v4i* a, const v4i
 }  // namespace
 
 // Operations one launch performs: 4 waves x iters x 2 097 152 per workgroup
-// (every mode issues 2^21 multiply-adds x 2 per wave and iteration).
+// (every mode issues 2^20 multiply-adds, 2^21 operations, per wave and
+// iteration).
 extern "C" double w8a8_probe_mfma_ops(int grid, int iters) {
   return static_cast<double>(grid) * 4.0 * iters * 2097152.0;
 }
