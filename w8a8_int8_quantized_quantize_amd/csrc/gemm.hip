@@ -245,17 +245,10 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// A uniform 64-bit value forced into scalar registers.  It also stops the
-// compiler from folding per-lane offsets into hoisted 64-bit vector addresses.
-__device__ __forceinline__ const int8_t* sgpr_ptr(const int8_t* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<const int8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// The same as a global-address-space pointer (its loads can then take the
-// scalar-base + 32-bit vector-offset form).
+// A uniform 64-bit address forced into scalar registers, as a global-address-
+// space pointer: its loads then take the scalar-base + 32-bit vector-offset
+// form, and the compiler cannot fold per-lane offsets into hoisted 64-bit
+// vector addresses.
 __device__ __forceinline__ const global_i8* sgpr_gptr(const int8_t* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
