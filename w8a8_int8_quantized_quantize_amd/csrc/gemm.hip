@@ -1288,6 +1288,7 @@ using C5 = Tile<64, 64, 2, 2, 128, 2, 32>;    // wave tile 32 x 32
 using C6 = Tile<16, 64, 1, 4, 128, 2, 16>;    // wave tile 16 x 16 (skinny M)
 using C7 = Tile<256, 192, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 96(n)
 using C9 = Tile<256, 256, 2, 2, 64, 4, 16>;   // C0 on 16x16x64 blocks, one k-step per stage
+using C10 = Tile<256, 192, 2, 2, 64, 4, 16>;  // C7 on 16x16x64 blocks
 
 const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 0.97f},
@@ -1300,6 +1301,7 @@ const ConfigInfo kConfigs[] = {
     {"bm256_bn192_bk64_s4_mf32", 256, 192, 256, 1, 0.92f},
     {"few_rows_splitk4_mf16", 16, 16, 256, 8, 0.10f},
     {"bm256_bn256_bk64_s4_mf16", 256, 256, 256, 1, 1.00f},
+    {"bm256_bn192_bk64_s4_mf16", 256, 192, 256, 1, 0.93f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kSkinny = 6;    // 16-row tiled kernel
@@ -1379,16 +1381,19 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
 // Tile configurations of the e4m3 GEMM: 64-byte K steps, so BK = 128 keeps
 // two steps per stage; bf16 output only.
 namespace {
-// (A 32-byte operand doubles the fragment registers, so the wave tiles are
-// 128 x 64 / 64 x 128 / 64 x 64, not the int8 kernel's 128 x 128.)
+// (A 32-byte operand doubles the fragment registers: with two 64-byte k-steps
+// per stage the wave tiles are limited to 128 x 64 / 64 x 128 / 64 x 64; with
+// one k-step per 64-deep stage the int8 kernel's 128 x 128 wave tile fits.)
 using F0 = Tile<256, 128, 2, 2, 128, 3, 32, true>;  // 3 x 48 KiB stages, spread refills
 using F1 = Tile<128, 256, 2, 2, 128, 3, 32, true>;  // 3 x 48 KiB stages
 using F2 = Tile<128, 128, 2, 2, 128, 4, 32, true>;  // 4 x 32 KiB stages
+using F3 = Tile<256, 256, 2, 2, 64, 4, 32, true>;   // 4 x 32 KiB stages, one k-step each
 const ConfigInfo kFp8Configs[] = {
     {"fp8_bm256_bn128_bk128_s3_mf32", 256, 128, 256, 1, 1.00f},
     {"fp8_bm128_bn256_bk128_s3_mf32", 128, 256, 256, 1, 1.00f},
     {"fp8_bm128_bn128_bk128_s4_mf32", 128, 128, 256, 1, 0.80f},
     {"fp8_few_rows_splitk4_mf16", 16, 16, 256, 8, 0.10f},
+    {"fp8_bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 1.03f},
 };
 constexpr int kFp8FewRows = 3;
 constexpr int kNumFp8Configs = sizeof(kFp8Configs) / sizeof(kFp8Configs[0]);
@@ -1427,6 +1432,7 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 1: return launch_cfg<F1, false>(a, stream);
     case 2: return launch_cfg<F2, false>(a, stream);
     case 3: return launch_few_rows<4, 1, false, true>(a, stream);
+    case 4: return launch_cfg<F3, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1444,6 +1450,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 7: return launch_cfg_out<C7>(a, out_int32, stream);
     case 8: return launch_few_rows_any(a, out_int32, stream);
     case 9: return launch_cfg_out<C9>(a, out_int32, stream);
+    case 10: return launch_cfg_out<C10>(a, out_int32, stream);
     default: return hipErrorInvalidValue;
   }
 }
