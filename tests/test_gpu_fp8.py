@@ -93,8 +93,9 @@ def test_quantize_weight_fp8_bit_exact(N, K):
     assert np.array_equal(host(q), qo)
 
 
+# (600, 700, 1024): ragged M and N with whole stages in K (interior and edge kernels)
 FSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
-           (257, 136, 384), (129, 257, 3072)]
+           (257, 136, 384), (129, 257, 3072), (600, 700, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", FSHAPES)

@@ -123,8 +123,10 @@ def test_gelu_quantize_every_finite_bf16_pattern():
 
 
 # -------------------------------------------------------------------- GEMM --
+# (600, 700, 1024): K a whole number of stages with ragged M and N, so that
+# every tiled configuration runs both its interior-tile and edge-tile kernels
 GSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
-           (257, 16, 16), (16, 1000, 3072), (129, 257, 144), (3, 200, 12304)]
+           (257, 16, 16), (16, 1000, 3072), (129, 257, 144), (3, 200, 12304), (600, 700, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", GSHAPES)

@@ -165,6 +165,13 @@ struct Tile {
   // 3+ stages: refill loads are spread over the stage after the one whose
   // buffer they refill (one slice per MFMA row)
   static constexpr bool kSpread = STAGES >= 3;
+  // Large tiles stage their epilogue's scales and bias in LDS (after the
+  // stages: s_w [BN] fp32, s_x [BM] fp32, bias [BN] bf16), loaded early in
+  // the tile's K loop, so the epilogue does not wait on global loads queued
+  // behind the next tile's first stages.
+  static constexpr bool kEpiLds = BM >= 128 && BN >= 128;
+  static constexpr int kEpiBytes = kEpiLds ? ((BN * 6 + BM * 4 + 255) / 256) * 256 : 0;
+  static constexpr int kEpiOffset = STAGES * kStage;
   static_assert(BK == 64 || BK == 128, "BK");
   static_assert(kSteps == 1 || kSteps % 2 == 0, "fragment sets alternate per k-step");
   static_assert(TM % MF == 0 && TN % MF == 0, "wave tile must be whole MFMA blocks");
@@ -174,7 +181,8 @@ struct Tile {
   // deeper pipelines count each wave's own loads in vmcnt waits, so every
   // wave must issue the same number per stage; 2-stage pipelines wait for 0
   static_assert(STAGES == 2 || kLoads % kWaves == 0, "uneven loads need a 2-stage pipeline");
-  static_assert(STAGES >= 2 && STAGES * kStage <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && STAGES * kStage + kEpiBytes <= 160 * 1024, "LDS budget");
+  static_assert(!kEpiLds || kWaves >= 3, "three waves load the epilogue's vectors");
 };
 
 // Store instructions one wave of the interior-tile bf16 epilogue issues: one
@@ -491,10 +499,13 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t 
 // (four consecutive columns per 16-byte s_w load and 8-byte bias load; both
 // vectors are aligned on this path), then each accumulator block is
 // dequantized and written as 8-byte runs.
-template <class C>
+// EPI: the tile's scales and bias were staged in LDS (stage_epilogue_vectors)
+// and are read from there; otherwise from global memory.
+template <class C, bool EPI = false>
 __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int64_t n0, int wn,
                                               int wm, int lane,
-                                              const typename C::Acc (&acc)[C::FN][C::FM]) {
+                                              const typename C::Acc (&acc)[C::FN][C::FM],
+                                              const int8_t* smem = nullptr) {
   constexpr int MF = C::MF;
   constexpr int G = C::Op::kGroups;
   const int lr = lane % MF, lq = lane / MF;
@@ -505,20 +516,47 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
   const uint16_t* bp = a.bias;
   asm volatile("" : "+s"(sxp), "+s"(swp), "+s"(bp));
   float sx[C::FM];
-#pragma unroll
-  for (int fj = 0; fj < C::FM; ++fj) sx[fj] = sxp[m0 + wm * C::TM + fj * MF + lr];
   float4 sw[C::FN][G];
   uint2 bb[C::FN][G];
   // no bias: every term is -0.0 (bf16 0x8000)
   const uint2 nobias = make_uint2(0x80008000u, 0x80008000u);
+  if constexpr (EPI) {
+    typedef __attribute__((address_space(3))) const int8_t lds_i8;
+    lds_i8* epi = (lds_i8*)(smem + C::kEpiOffset);  // address-space cast
+    typedef __attribute__((address_space(3))) const float lds_f32;
+    typedef __attribute__((address_space(3))) const v4f lds_f32x4;
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) const v2u lds_u32x2;
+    lds_f32* lsx = reinterpret_cast<lds_f32*>(epi + C::BN * 4);
+    // the bias words are read whether or not there is a bias (the area then
+    // holds stale bytes) and replaced by -0.0 with a bit mask: a choice
+    // between loading and not loading would become a choice of address,
+    // which loses the LDS address space
+    const uint32_t keep = bp ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-  for (int fi = 0; fi < C::FN; ++fi)
+    for (int fj = 0; fj < C::FM; ++fj) sx[fj] = lsx[wm * C::TM + fj * MF + lr];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
-      sw[fi][g] = *reinterpret_cast<const float4*>(swp + n);
-      bb[fi][g] = bp ? *reinterpret_cast<const uint2*>(bp + n) : nobias;
-    }
+    for (int fi = 0; fi < C::FN; ++fi)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int c = wn * C::TN + fi * MF + lq * 4 + g * 8;
+        const v4f w = *reinterpret_cast<lds_f32x4*>(epi + c * 4);
+        sw[fi][g] = make_float4(w[0], w[1], w[2], w[3]);
+        const v2u v = *reinterpret_cast<lds_u32x2*>(epi + C::BN * 4 + C::BM * 4 + c * 2);
+        bb[fi][g] = make_uint2((v[0] & keep) | (nobias.x & ~keep), (v[1] & keep) | (nobias.y & ~keep));
+      }
+  } else {
+#pragma unroll
+    for (int fj = 0; fj < C::FM; ++fj) sx[fj] = sxp[m0 + wm * C::TM + fj * MF + lr];
+#pragma unroll
+    for (int fi = 0; fi < C::FN; ++fi)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
+        sw[fi][g] = *reinterpret_cast<const float4*>(swp + n);
+        bb[fi][g] = bp ? *reinterpret_cast<const uint2*>(bp + n) : nobias;
+      }
+  }
   uint16_t* y = static_cast<uint16_t*>(a.out);
   // group g of block (fi, fj), dequantized and packed to 4 bf16
   auto pack = [&](int fi, int fj, int g) {
@@ -760,6 +798,37 @@ __device__ __forceinline__ void stage_steps(const Loader<C, FAST>& ld, Frags<C> 
 }
 
 
+// The tile's epilogue vectors into LDS, one direct-to-LDS load per wave
+// (16 bytes per lane): wave 0 the BN scales s_w, wave 1 the BM scales s_x,
+// wave 2 the BN bf16 biases (none without a bias).  Issued after the tile's
+// first barrier (every wave is done with the previous tile's epilogue) and
+// before the loads of its stage S - 1 (spread) or 2 (two stages), so the
+// K loop's wait for those loads and its next barrier also make these visible
+// to every wave; tiles with too few stages for that wait explicitly.
+template <class C>
+__device__ __forceinline__ void stage_epilogue_vectors(const GemmArgs& a, int8_t* smem, int64_t m0,
+                                                       int64_t n0, int wave, int lane) {
+  int8_t* epi = smem + C::kEpiOffset;
+  const int8_t* src = nullptr;
+  int bytes = 0, dst = 0;
+  if (wave == 0) {
+    src = reinterpret_cast<const int8_t*>(a.sw + n0);
+    bytes = C::BN * 4;
+  } else if (wave == 1) {
+    src = reinterpret_cast<const int8_t*>(a.sx + m0);
+    bytes = C::BM * 4;
+    dst = C::BN * 4;
+  } else if (wave == 2 && a.bias != nullptr) {
+    src = reinterpret_cast<const int8_t*>(a.bias + n0);
+    bytes = C::BN * 2;
+    dst = C::BN * 4 + C::BM * 4;
+  }
+  if (lane * 16 < bytes) {
+    const global_i8* g = sgpr_gptr(src) + lane * 16;
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(epi + dst), 16, 0, 0);
+  }
+}
+
 // Stages the prologue of a tile loads before its K loop.  Every wave issues
 // the same load sequence whatever KST is: the prologue stages and each
 // stage's refill always go out.  Spread pipelines prefetch S - 1 stages
@@ -796,7 +865,7 @@ __device__ __forceinline__ void tile_prologue(const GemmArgs& a, int8_t* smem, i
 // was measured slower: more L2 misses.)  Loads and stores return in issue
 // order, so the first wait below also covers stores the previous tile's
 // epilogue issued after this tile's first loads.
-template <class C, bool FAST>
+template <class C, bool FAST, bool EPI = false>
 __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, int64_t m0,
                                               int64_t n0, int ph, bool chain, int64_t m1,
                                               int64_t n1, bool stored, int wave, int lane,
@@ -841,6 +910,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
       wait_stages<C>(PRO - 1);
     }
     block_barrier();
+    if constexpr (EPI) stage_epilogue_vectors<C>(a, smem, m0, n0, wave, lane);
     Frags<C> f[2];
     read_frags<C>(f[0], buf(0), lw[0], lx[0]);
     // nothing in flight on the LDS / scalar-load counter when the K loop
@@ -980,23 +1050,36 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
   }
 }
 
-template <class C, bool FAST, bool OUT_I32>
+template <class C, bool FAST, bool OUT_I32, bool EPI = false>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int64_t m0, int64_t n0, int wave,
-                                              int lane, const typename C::Acc (&acc)[C::FN][C::FM]) {
+                                              int lane, const typename C::Acc (&acc)[C::FN][C::FM],
+                                              const int8_t* smem = nullptr) {
   const int wn = wave % C::WN, wm = wave / C::WN;
   if constexpr (FAST && !OUT_I32)
-    epilogue_fast<C>(a, m0, n0, wn, wm, lane, acc);
+    epilogue_fast<C, EPI>(a, m0, n0, wn, wm, lane, acc, smem);
   else
     epilogue<C, OUT_I32, !FAST>(a, m0, n0, wn, wm, lane, acc);
 }
 
-template <class C>
-__device__ __forceinline__ bool tile_is_fast(const GemmArgs& a, int64_t m0, int64_t n0) {
-  // interior tile, whole stages in K, 16-byte output rows, and vector-aligned
-  // scales / bias
-  return (m0 + C::BM <= a.M) && (n0 + C::BN <= a.N) && (a.N % 8 == 0) && (a.K % C::BK == 0) &&
-         (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
-         (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0);
+// Tiles of the edge kernel, e in [0, E): the last row of tiles when M is
+// ragged (every column), then the last column when N is ragged (the rows
+// above it); or, with `all`, every tile (row-major) when no tile can take the
+// unguarded path.
+__device__ __forceinline__ void edge_coords(int e, int MT, int NT, int MTi, int NTi, bool all,
+                                            int& tm, int& tn) {
+  if (all) {
+    tm = e / NT;
+    tn = e - tm * NT;
+    return;
+  }
+  const int nrow = MT > MTi ? NT : 0;
+  if (e < nrow) {
+    tm = MTi;
+    tn = e;
+    return;
+  }
+  tm = e - nrow;
+  tn = NTi;
 }
 
 // Persistent workgroups: workgroup b takes tiles b, b + G, b + 2G, ... (G =
@@ -1004,21 +1087,38 @@ __device__ __forceinline__ bool tile_is_fast(const GemmArgs& a, int64_t m0, int6
 // each workgroup stays on one XCD's tile range).  The next tile's prologue
 // loads go out before the current tile's epilogue, so their latency hides
 // behind its arithmetic and stores.
-template <class C, bool OUT_I32>
-__global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, int MT, int NT) {
-  __shared__ __attribute__((aligned(1024))) int8_t smem[C::STAGES * C::kStage];
+// Two kernels per configuration: the interior one (EDGE = false) takes the
+// MTi x NTi tiles that lie wholly inside M and N -- the host launches it only
+// when K is a whole number of stages, output rows are multiples of 16 bytes
+// and the scales / bias are vector aligned -- with unguarded loads, chained
+// tiles and the vector epilogue; the edge one takes the remaining tiles with
+// clamped loads and guarded stores.  Kept apart, the interior kernel holds no
+// registers for the guarded code: it does not spill, so no reload (and no
+// wait for all outstanding loads that a reload implies) sits between a tile's
+// K loop and its epilogue while the next tile's first stages are in flight.
+template <class C, bool OUT_I32, bool EDGE>
+__global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, int MT, int NT,
+                                                           int MTi, int NTi, int all) {
+  constexpr bool FAST = !EDGE;
+  // interior bf16 tiles of large configurations stage their epilogue vectors
+  constexpr bool EPI = FAST && !OUT_I32 && C::kEpiLds;
+  __shared__ __attribute__((aligned(1024))) int8_t smem[C::STAGES * C::kStage + (EPI ? C::kEpiBytes : 0)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int t = blockIdx.x;
   if (t >= T) return;
-  int tm, tn;
-  tile_coords(t, T, MT, NT, tm, tn);
-  int64_t m0 = static_cast<int64_t>(tm) * C::BM, n0 = static_cast<int64_t>(tn) * C::BN;
-  bool fast = tile_is_fast<C>(a, m0, n0);
-  if (fast)
-    tile_prologue<C, true>(a, smem, m0, n0, wave, lane);
-  else
-    tile_prologue<C, false>(a, smem, m0, n0, wave, lane);
+  auto origin = [&](int tt, int64_t& m, int64_t& n) {
+    int tm, tn;
+    if constexpr (EDGE)
+      edge_coords(tt, MT, NT, MTi, NTi, all != 0, tm, tn);
+    else
+      tile_coords(tt, T, MTi, NTi, tm, tn);
+    m = static_cast<int64_t>(tm) * C::BM;
+    n = static_cast<int64_t>(tn) * C::BN;
+  };
+  int64_t m0, n0;
+  origin(t, m0, n0);
+  tile_prologue<C, FAST>(a, smem, m0, n0, wave, lane);
   const int KST = static_cast<int>((a.K + C::BK - 1) / C::BK);
   int ph = 0;       // LDS buffer of the current tile's stage 0
   bool stored = false;  // see tile_mainloop
@@ -1027,25 +1127,24 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
     const int tnext = t + static_cast<int>(gridDim.x);
     const bool more = tnext < T;
     int64_t m1 = 0, n1 = 0;
-    bool fast1 = false;
-    if (more) {
-      tile_coords(tnext, T, MT, NT, tm, tn);
-      m1 = static_cast<int64_t>(tm) * C::BM;
-      n1 = static_cast<int64_t>(tn) * C::BN;
-      fast1 = tile_is_fast<C>(a, m1, n1);
-    }
+    if (more) origin(tnext, m1, n1);
     // interior tiles chain: this tile's last refills are the next one's
     // first stages
-    const bool chain = C::kSpread && fast && fast1 && KST > 0;
+    const bool chain = FAST && C::kSpread && more && KST > 0;
     // opaque per tile: lane- and wave-derived offsets are recomputed for
     // each tile instead of being hoisted out of the tile loop, where their
     // registers would be held through every K loop
     int ln = lane, wv = wave;
     asm volatile("" : "+v"(ln), "+s"(wv));
-    if (fast)
-      tile_mainloop<C, true>(a, smem, m0, n0, ph, chain, m1, n1, stored, wv, ln, acc);
-    else
-      tile_mainloop<C, false>(a, smem, m0, n0, ph, false, m1, n1, stored, wv, ln, acc);
+    tile_mainloop<C, FAST, EPI>(a, smem, m0, n0, ph, chain, m1, n1, stored, wv, ln, acc);
+    if constexpr (EPI) {
+      // too few stages for the K loop's waits and barriers to cover the
+      // epilogue vectors: wait for them explicitly (K <= STAGES x BK)
+      if (KST <= C::STAGES) {
+        wait_vm0();
+        block_barrier();
+      }
+    }
     if (chain) {
       ph = (ph + KST) % C::STAGES;
     } else if (more) {
@@ -1053,25 +1152,18 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
       block_barrier();  // every wave is done reading this tile's LDS buffers
       int ln1 = lane, wv1 = wave;
       asm volatile("" : "+v"(ln1), "+s"(wv1));
-      if (fast1)
-        tile_prologue<C, true>(a, smem, m1, n1, wv1, ln1);
-      else
-        tile_prologue<C, false>(a, smem, m1, n1, wv1, ln1);
+      tile_prologue<C, FAST>(a, smem, m1, n1, wv1, ln1);
     }
     int ln2 = lane, wv2 = wave;
     asm volatile("" : "+v"(ln2), "+s"(wv2));
-    if (fast)
-      tile_epilogue<C, true, OUT_I32>(a, m0, n0, wv2, ln2, acc);
-    else
-      tile_epilogue<C, false, OUT_I32>(a, m0, n0, wv2, ln2, acc);
+    tile_epilogue<C, FAST, OUT_I32, EPI>(a, m0, n0, wv2, ln2, acc, smem);
     // the next tile's first stages went out before these stores; the
     // interior bf16 epilogue issues exactly kFastStores of them
-    stored = fast && !OUT_I32;
+    stored = FAST && !OUT_I32;
     if (!more) break;
     t = tnext;
     m0 = m1;
     n0 = n1;
-    fast = fast1;
   }
 }
 
@@ -1308,26 +1400,60 @@ constexpr int kSkinny = 6;    // 16-row tiled kernel
 constexpr int kFewRows = 8;   // split-K few-row kernel
 constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
+// Persistent grid: as many workgroups of `kernel` as fit on the device at
+// once (a multiple of the 8 XCDs), or one per tile if there are fewer tiles.
+template <class K>
+hipError_t persistent_grid(K kernel, int threads, int64_t tiles, int& grid) {
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+  if (e != hipSuccess) return e;
+  int64_t resident = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : 1);
+  resident = resident >= 8 ? (resident / 8) * 8 : resident;
+  grid = static_cast<int>(tiles < resident ? tiles : resident);
+  return hipSuccess;
+}
+
 template <class C, bool I32>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t MT = (a.M + C::BM - 1) / C::BM;
   const int64_t NT = (a.N + C::BN - 1) / C::BN;
-  const int64_t T = MT * NT;
-  if (T > INT32_MAX) return hipErrorInvalidValue;
-  // Persistent grid: as many workgroups as fit on the device at once (a
-  // multiple of the 8 XCDs), or one per tile if there are fewer tiles.
-  int dev = 0, cus = 0, per_cu = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_kernel<C, I32>, C::kThreads, 0);
-  if (e != hipSuccess) return e;
-  int64_t resident = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : 1);
-  resident = resident >= 8 ? (resident / 8) * 8 : resident;
-  const int grid = static_cast<int>(T < resident ? T : resident);
-  gemm_kernel<C, I32><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
-      a, static_cast<int>(T), static_cast<int>(MT), static_cast<int>(NT));
-  return hipGetLastError();
+  if (MT * NT > INT32_MAX) return hipErrorInvalidValue;
+  // the interior kernel's conditions: whole stages in K, 16-byte output rows,
+  // vector-aligned scales and bias; then every tile wholly inside M and N
+  // takes it, and the edge kernel the rest
+  // (configurations that stage their epilogue vectors in LDS also need K > 0
+  // and 16-byte aligned s_x and bias for the 16-byte direct-to-LDS loads)
+  const bool epi = C::kEpiLds && !I32;
+  const bool interior = (a.N % 8 == 0) && (a.K % C::BK == 0) &&
+                        (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
+                        (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0) &&
+                        (!epi || (a.K > 0 && reinterpret_cast<uintptr_t>(a.sx) % 16 == 0 &&
+                                  reinterpret_cast<uintptr_t>(a.bias) % 16 == 0));
+  const int64_t MTi = interior ? a.M / C::BM : 0;
+  const int64_t NTi = interior ? a.N / C::BN : 0;
+  const int64_t Ti = MTi * NTi;
+  const int64_t E = interior ? (MT > MTi ? NT : 0) + (NT > NTi ? MTi : 0) : MT * NT;
+  int grid = 0;
+  if (Ti > 0) {
+    hipError_t e = persistent_grid(gemm_kernel<C, I32, false>, C::kThreads, Ti, grid);
+    if (e != hipSuccess) return e;
+    gemm_kernel<C, I32, false><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
+        a, static_cast<int>(Ti), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),
+        static_cast<int>(NTi), 0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (E > 0) {
+    hipError_t e = persistent_grid(gemm_kernel<C, I32, true>, C::kThreads, E, grid);
+    if (e != hipSuccess) return e;
+    gemm_kernel<C, I32, true><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
+        a, static_cast<int>(E), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),
+        static_cast<int>(NTi), interior ? 0 : 1);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 template <class C>
