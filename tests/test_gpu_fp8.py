@@ -93,9 +93,10 @@ def test_quantize_weight_fp8_bit_exact(N, K):
     assert np.array_equal(host(q), qo)
 
 
-# (600, 700, 1024): ragged M and N with whole stages in K (interior and edge kernels)
+# (600, 700, 1024): ragged M and N with whole stages in K (interior and edge
+# kernels); (520, 530, 256): interior tiles with no more K stages than buffers
 FSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
-           (257, 136, 384), (129, 257, 3072), (600, 700, 1024)]
+           (257, 136, 384), (129, 257, 3072), (600, 700, 1024), (520, 530, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", FSHAPES)
@@ -160,7 +161,7 @@ def test_full_size_linear_fp8_sampled(shape):
     assert_fp8_gemm_bound(bits(y)[rows], qx, sx, qw, sw, bb, shape.name)
 
 
-@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (4, 48)])
+@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (4, 48), (4133, 3072)])
 def test_gelu_quantize_fp8_teacher_forced(M, K):
     rng = np.random.default_rng(M + 5 * K)
     yb = rand_bits(rng, M, K, scale=3.0, outliers=max(1, K // 100))

@@ -87,7 +87,10 @@ def test_quantize_weight_bit_exact(N, K):
     assert np.array_equal(host(q), qo)
 
 
-@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (2, 16384), (4, 48)])
+# large M: the persistent grid of 256 workgroups x 16 waves (one row per wave
+# at a time) covers 4096 rows per pass; 4133 and 6000 take a second, partial pass
+@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (2, 16384), (4, 48),
+                                 (4133, 3072), (6000, 1040), (4096, 12288)])
 def test_gelu_quantize_teacher_forced(M, K):
     rng = np.random.default_rng(M + 3 * K)
     yb = rand_bits(rng, M, K, scale=3.0, outliers=max(1, K // 100))
@@ -124,9 +127,12 @@ def test_gelu_quantize_every_finite_bf16_pattern():
 
 # -------------------------------------------------------------------- GEMM --
 # (600, 700, 1024): K a whole number of stages with ragged M and N, so that
-# every tiled configuration runs both its interior-tile and edge-tile kernels
+# every tiled configuration runs both its interior-tile and edge-tile kernels;
+# (520, 530, 256) and (520, 530, 128): interior tiles with no more K stages
+# than LDS buffers (their epilogue vectors are waited for explicitly)
 GSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
-           (257, 16, 16), (16, 1000, 3072), (129, 257, 144), (3, 200, 12304), (600, 700, 1024)]
+           (257, 16, 16), (16, 1000, 3072), (129, 257, 144), (3, 200, 12304), (600, 700, 1024),
+           (520, 530, 256), (520, 530, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", GSHAPES)
