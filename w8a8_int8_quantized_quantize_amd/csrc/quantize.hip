@@ -111,19 +111,21 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Code of x as the low byte of the returned word.  MODE 0: s == 0 (all
-// zero); MODE 1: IEEE division; MODE 2: reciprocal + Markstein correction.
+// zero); MODE 1: IEEE division, clamped to [-127, 127] (a subnormal scale can
+// be far below absmax / 127); MODE 2: reciprocal + Markstein correction, no
+// clamp: there s >= 2^-96 is within 2^-24 of absmax / 127, so |x / s| for
+// |x| <= absmax stays below 127.5 and rounds into [-127, 127] by itself.
 template <int MODE>
 __device__ __forceinline__ uint32_t code_word(float x, float s, float r) {
   float t;
   if constexpr (MODE == 0) {
     return 0u;
   } else if constexpr (MODE == 1) {
-    t = x / s;
+    t = __builtin_amdgcn_fmed3f(x / s, -127.0f, 127.0f);
   } else {
     const float q = x * r;
     t = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
   }
-  t = __builtin_amdgcn_fmed3f(t, -127.0f, 127.0f);
   return __float_as_uint(t + 12582912.0f);
 }
 
@@ -334,12 +336,24 @@ __device__ __forceinline__ void stage_lut(uint16_t* lut) {
   }
 }
 
-// GELU through the staged table, absmax, optional h copy, codes.
+// Rows of a workgroup in flight: the wave holding the workgroup's i-th row
+// (i = wave + 16 n for its n-th row) issues that row's loads once at least
+// i - depth + 1 of the workgroup's rows have arrived, as counted in LDS.
+// Rows increase with i, so every row before a waiting one exists and is
+// counted once its own (earlier) wait has ended: every wait ends.
+__device__ __forceinline__ void wait_rows_arrived(const int* arrived, int need) {
+  while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < need)
+    __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// GELU through the staged table, absmax (counting the row as arrived once
+// its last chunk has been read), optional h copy, codes.
 template <int CH, bool FP8>
 __device__ __forceinline__ void gelu_finish_row(const uint16_t* lut, uint4 (&raw)[CH], int64_t row,
                                                 int64_t K, uint32_t nch, uint32_t ln, int lane,
                                                 int8_t* q, int64_t ldq, float* scale,
-                                                uint16_t* h_out) {
+                                                uint16_t* h_out, int* arrived) {
   u16x2 m = {0, 0};
   Gather8 cur;
   cur.issue(lut, raw[0]);
@@ -352,6 +366,7 @@ __device__ __forceinline__ void gelu_finish_row(const uint16_t* lut, uint4 (&raw
     cur = nxt;
     __builtin_amdgcn_sched_barrier(0);  // at most two chunks' gathers at a time
   }
+  if (lane == 0) __hip_atomic_fetch_add(arrived, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   if (h_out != nullptr) {
     uint4* hrow = reinterpret_cast<uint4*>(h_out + row * K);
 #pragma unroll
@@ -366,19 +381,30 @@ __device__ __forceinline__ void gelu_finish_row(const uint16_t* lut, uint4 (&raw
   emit_bf16_row<CH, FP8>(raw, mode, s, r, nch, ln, q + row * ldq);
 }
 
+// depth: rows of the workgroup in flight (1..16).  At most `depth` rows
+// per compute unit are being read at a time, so rows arrive one after
+// another and their codes are computed while later rows stream in, instead
+// of every row's data landing at the end of one long read phase.
 template <int CH, bool FP8>
 __global__ __launch_bounds__(kLutThreads) void gelu_quantize_regs(
     const uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t ldy, int8_t* __restrict__ q,
-    int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
+    int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out, int depth) {
   __shared__ __attribute__((aligned(1024))) uint16_t lut[65536];
+  __shared__ int arrived;
   const int lane = threadIdx.x & 63;
-  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  const int wave = wave_id();
+  const uint32_t nch = static_cast<uint32_t>(K / 8);  // K >= 16: nch >= 2
   const int64_t stride = (int64_t)gridDim.x * kLutWaves;
-  int64_t row = (int64_t)blockIdx.x * kLutWaves + wave_id();
+  int64_t row = (int64_t)blockIdx.x * kLutWaves + wave;
+  int item = wave;  // position of `row` in the workgroup's row sequence
+  if (wave == 0) {
+    if (lane == 0) arrived = 0;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the store is in LDS before the barrier
+  }
   stage_lut(lut);
-  // First row, peeled: its loads go out while the table pieces are in
-  // flight.  Every wave reaches a barrier, also one without a row.
-  if (row < M && nch > 0) {
+  if (row < M && wave < depth) {
+    // First rows, peeled: their loads go out while the table pieces are in
+    // flight.  Every wave reaches the barrier, also one without a row.
     uint4 raw[CH];
     __builtin_amdgcn_sched_barrier(0);
     load_row<CH>(reinterpret_cast<const uint4*>(y + row * ldy), nch, lane, raw);
@@ -386,22 +412,20 @@ __global__ __launch_bounds__(kLutThreads) void gelu_quantize_regs(
     wait_vmcnt<CH>();   // loads complete in order: the older table pieces have landed
     __builtin_amdgcn_s_barrier();  // ... and so have every other wave's
     __builtin_amdgcn_sched_barrier(0);
-    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
+    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out, &arrived);
+    row += stride;
+    item += kLutWaves;
   } else {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (row >= M) return;
-    uint4 raw[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) raw[j] = make_uint4(0u, 0u, 0u, 0u);
-    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, lane, lane, q, ldq, scale, h_out);
   }
-  for (row += stride; row < M; row += stride) {
+  for (; row < M; row += stride, item += kLutWaves) {
+    wait_rows_arrived(&arrived, item - depth + 1);
     uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
     asm volatile("" : "+v"(ln));   // from being hoisted into live registers
     uint4 raw[CH];
     load_row<CH>(reinterpret_cast<const uint4*>(y + row * ldy), nch, ln, raw);
-    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, ln, lane, q, ldq, scale, h_out);
+    gelu_finish_row<CH, FP8>(lut, raw, row, K, nch, ln, lane, q, ldq, scale, h_out, &arrived);
   }
 }
 
@@ -515,15 +539,28 @@ hipError_t launch_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
   return hipGetLastError();
 }
 
+// Rows per GELU workgroup in flight: about 192 KiB of row data per compute
+// unit, at least 4 rows and at most one per wave.  For K = 12288 that is 8
+// rows: on MI355X, 4096 such rows take 31.9 us with 8 in flight against
+// 34.3 us with all 16 (one row per wave, all loads at once) and 32.0-34.4 us
+// with 3, 4 or 6.
+int gelu_rows_in_flight(int64_t K) {
+  const int64_t row_bytes = 2 * K;
+  const int64_t d = (192 * 1024 + row_bytes - 1) / row_bytes;
+  return static_cast<int>(std::max<int64_t>(4, std::min<int64_t>(d, kLutWaves)));
+}
+
 template <bool FP8>
 hipError_t launch_gelu(const uint16_t* y, int64_t M, int64_t K, int64_t ldy, int8_t* q,
                        int64_t ldq, float* scale, uint16_t* h_out, hipStream_t stream) {
   const int64_t per_lane = (K / 8 + 63) / 64;
   const int64_t blocks = std::min<int64_t>((M + kLutWaves - 1) / kLutWaves, kLutMaxBlocks);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kLutThreads);
+  const int depth = gelu_rows_in_flight(K);
 #define W8A8_G_CASE(CHV)                                                                     \
-  if (K > 0 && per_lane <= CHV) {                                                                     \
-    gelu_quantize_regs<CHV, FP8><<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out); \
+  if (K > 0 && per_lane <= CHV) {                                                            \
+    gelu_quantize_regs<CHV, FP8>                                                             \
+        <<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out, depth);            \
     return hipGetLastError();                                                                \
   }
   W8A8_FOR_CH(W8A8_G_CASE)
