@@ -161,7 +161,8 @@ def test_full_size_linear_fp8_sampled(shape):
     assert_fp8_gemm_bound(bits(y)[rows], qx, sx, qw, sw, bb, shape.name)
 
 
-@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (4, 48), (4133, 3072)])
+@pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (4, 48), (4133, 3072),
+                                 (4500, 12288), (700, 10240)])
 def test_gelu_quantize_fp8_teacher_forced(M, K):
     rng = np.random.default_rng(M + 5 * K)
     yb = rand_bits(rng, M, K, scale=3.0, outliers=max(1, K // 100))
