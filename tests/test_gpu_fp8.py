@@ -121,6 +121,25 @@ def test_gemm_fp8_every_config_within_bound(M, N, K, with_bias):
     assert_fp8_gemm_bound(y, qx, sx, qw, sw, bb, f"linear {M}x{N}x{K}")
 
 
+# More interior tiles than persistent workgroups (M = 4096, N = 4352: 272 to
+# 1088 interior tiles by configuration): workgroups run several tiles in a
+# row, with K from one LDS stage to several.
+@pytest.mark.parametrize("K", [64, 128, 256, 384])
+def test_gemm_fp8_consecutive_interior_tiles_every_config(K):
+    M, N = 4096, 4352
+    rng = np.random.default_rng(7 * K)
+    xb = rand_bits(rng, M, K, outliers=1)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0]
+    qx, sx = oracle.quantize_rows_bf16_fp8(xb)
+    qw, sw = oracle.quantize_rows_f32_fp8(w)
+    dq, dsx = torch.from_numpy(qx).to(DEV), torch.from_numpy(sx).to(DEV)
+    dw, dsw = torch.from_numpy(qw).to(DEV), torch.from_numpy(sw).to(DEV)
+    for c in range(w8.w8a8_gemm_fp8_num_configs()):
+        y = bits(w8.w8a8_gemm_dequant_fp8(dq, dsx, dw, dsw, dev_bf16(bb), config=c))
+        assert_fp8_gemm_bound(y, qx, sx, qw, sw, bb, f"{M}x{N}x{K} {w8.w8a8_gemm_fp8_config_name(c)}")
+
+
 def test_gemm_fp8_extremes_and_k_zero():
     # all codes +-448: sums of 448^2 products (exact in fp32 up to K = 256)
     M, N, K = 40, 72, 256

@@ -190,6 +190,35 @@ def test_linear_bf16_parity_every_config(M, N, K, with_bias):
         assert np.array_equal(bits(yc), want["y"]), w8.w8a8_gemm_config_name(c)
 
 
+# More interior tiles than persistent workgroups (M = 4096, N = 4352: 272 to
+# 1088 interior tiles by configuration), so workgroups run several tiles in a
+# row, with K from one LDS stage (tiles too short to prefetch the next tile's
+# first stages from their own refills) to several.
+@pytest.mark.parametrize("K", [64, 128, 192, 320])
+def test_consecutive_interior_tiles_every_config(K):
+    M, N = 4096, 4352
+    rng = np.random.default_rng(K)
+    a = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    b = rng.integers(-127, 128, (N, K)).astype(np.int8)
+    want = oracle.gemm_i64(a, b)
+    qa, qb = torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV)
+    for c in range(ncfg()):
+        g = host(w8.w8a8_gemm_ex(qa, None, qb, None, out_int32=True, config=c))
+        assert np.array_equal(g.astype(np.int64), want), w8.w8a8_gemm_config_name(c)
+    xb = rand_bits(rng, M, K, outliers=1)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0]
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    wqo, swo = oracle.quantize_rows_f32(w)
+    assert np.array_equal(host(wq), wqo) and np.array_equal(host(sw), swo)
+    yo = oracle.linear(xb, wqo, swo, bb)["y"]
+    q, s = w8.w8a8_quantize_act(dev_bf16(xb))
+    bias = dev_bf16(bb)
+    for c in range(ncfg()):
+        yc = w8.w8a8_gemm_ex(q, s, wq, sw, bias, config=c)
+        assert np.array_equal(bits(yc), yo), w8.w8a8_gemm_config_name(c)
+
+
 def test_linear_k_zero_is_bias_and_empty_batches():
     N = 40
     rng = np.random.default_rng(5)

@@ -1129,8 +1129,11 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
     int64_t m1 = 0, n1 = 0;
     if (more) origin(tnext, m1, n1);
     // interior tiles chain: this tile's last refills are the next one's
-    // first stages
-    const bool chain = FAST && C::kSpread && more && KST > 0;
+    // first stages.  Stage st refills stage st + S - 1, so the refills reach
+    // the next tile's stages 0 .. S - 2 only when the tile has at least S - 1
+    // stages; shorter tiles load the next tile's prologue after their K loop
+    // (with clamped stage indices) instead.
+    const bool chain = FAST && C::kSpread && more && KST >= C::STAGES - 1;
     // opaque per tile: lane- and wave-derived offsets are recomputed for
     // each tile instead of being hoisted out of the tile loop, where their
     // registers would be held through every K loop
