@@ -38,9 +38,13 @@ def bf16_vals(b: np.ndarray) -> np.ndarray:
     return oracle.bf16_to_f32(b).astype(np.float64)
 
 
-def assert_fp8_gemm_bound(y_bits, q_x, s_x, q_w, s_w, bias_bits, what=""):
-    acc = oracle.gemm_fp8(q_x, q_w)
-    mag = oracle.gemm_fp8(q_x & 0x7F, q_w & 0x7F)  # sum_k |a_k b_k|, exact
+def fp8_exact_sums(q_x, q_w):
+    """The exact products a q_x @ q_w^T and their magnitudes sum_k |a_k b_k|."""
+    return oracle.gemm_fp8(q_x, q_w), oracle.gemm_fp8(q_x & 0x7F, q_w & 0x7F)
+
+
+def assert_fp8_gemm_bound(y_bits, q_x, s_x, q_w, s_w, bias_bits, what="", sums=None):
+    acc, mag = sums if sums is not None else fp8_exact_sums(q_x, q_w)
     f = s_x.astype(np.float64)[:, None] * s_w.astype(np.float64)[None, :]
     yv = f * acc + (bf16_vals(bias_bits)[None, :] if bias_bits is not None else 0.0)
     got = bf16_vals(y_bits)
@@ -135,9 +139,11 @@ def test_gemm_fp8_consecutive_interior_tiles_every_config(K):
     qw, sw = oracle.quantize_rows_f32_fp8(w)
     dq, dsx = torch.from_numpy(qx).to(DEV), torch.from_numpy(sx).to(DEV)
     dw, dsw = torch.from_numpy(qw).to(DEV), torch.from_numpy(sw).to(DEV)
+    sums = fp8_exact_sums(qx, qw)
     for c in range(w8.w8a8_gemm_fp8_num_configs()):
         y = bits(w8.w8a8_gemm_dequant_fp8(dq, dsx, dw, dsw, dev_bf16(bb), config=c))
-        assert_fp8_gemm_bound(y, qx, sx, qw, sw, bb, f"{M}x{N}x{K} {w8.w8a8_gemm_fp8_config_name(c)}")
+        assert_fp8_gemm_bound(y, qx, sx, qw, sw, bb, f"{M}x{N}x{K} {w8.w8a8_gemm_fp8_config_name(c)}",
+                              sums)
 
 
 def test_gemm_fp8_extremes_and_k_zero():
