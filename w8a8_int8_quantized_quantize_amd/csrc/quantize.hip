@@ -25,15 +25,18 @@
 // It is used for rows with s >= 2^-96, where an exhaustive check over every
 // pair of bf16 values |x| <= absmax confirms it (the residual e stays in the
 // normal range there); smaller scales, and fp32 rows, use the IEEE division.
-// Rounding: clamp to [-127, 127] (v_med3), then adding 1.5 * 2^23 rounds to
-// an integer, half to even, whose two's-complement byte is the low byte of the
-// sum's bit pattern.
+// Rounding: adding 1.5 * 2^23 rounds to an integer, half to even, whose
+// two's-complement byte is the low byte of the sum's bit pattern; the
+// division path clamps to [-127, 127] (v_med3) first, the reciprocal path
+// needs no clamp (its quotients stay below 127.5 in magnitude).
 //
 // GELU: the input is bf16, so gelu is a function on 65536 patterns; its
 // correctly rounded bf16 values form a 128 KiB table (written at build time by
 // gen_gelu_lut.py in double precision) that every workgroup stages in LDS
 // with direct-to-LDS loads.  One workgroup of 16 waves per CU (the table fills
 // 128 KiB of the 160 KiB of LDS); each element then costs one LDS gather.
+// A workgroup keeps a bounded number of rows in flight, so that rows land one
+// after another and their codes overlap the reads of later rows.
 //
 // Exactness: built with correctly rounded fp32 division, fp32 denormals kept
 // and contraction off, so every step matches the IEEE definition bit for bit.
