@@ -4,24 +4,27 @@
 One step = one pass of the whole hot path over the 1024px DiT MLP workload
 (4096 tokens, hidden 3072, MLP width 12288), on synthetic seeded inputs that
 are resident in HBM before timing starts:
-  1. per-token quantization of the up-proj input X [4096, 3072]
-  2. int8 GEMM + dequant/bias epilogue, up-proj   (M=4096, K=3072,  N=12288)
-  3. GELU + per-token quantization of the up-proj output [4096, 12288]
-  4. int8 GEMM + dequant/bias epilogue, down-proj (M=4096, K=12288, N=3072)
-Steps 1+2 are exactly what w8a8_linear enqueues; they are issued as the two
-entry points so that HIP events can bracket the GEMM kernel alone.  Weight
-quantization (per output channel) is offline and not timed.  Weights rotate
-over several copies so that the 256 MB last-level cache cannot hold them
-across steps.
+  1. the fused linear w8a8_linear, up-proj (M=4096, K=3072, N=12288):
+     per-token quantization of X into its workspace, then the int8 GEMM with
+     the dequant/bias epilogue
+  2. GELU + per-token quantization of the up-proj output [4096, 12288]
+  3. int8 GEMM + dequant/bias epilogue, down-proj (M=4096, K=12288, N=3072)
+Weight quantization (per output channel) is offline and not timed.  Weights
+rotate over several copies so that the 256 MB last-level cache cannot hold
+them across steps.
 
 Output: one JSON line.  `value` is int8 tera-operations per second over the
-whole step (2*M*N*K per GEMM).  `roofline` reports the up-proj GEMM kernel
-(the headline shape) against the 5.0 POP/s dense int8 matrix peak, timed with
-a HIP event pair around it on the stream the kernels run on, in every timed
-step.  The timed steps record only that pair: each recorded event costs the
-step ~3 us, so `kernels_ms` (every kernel bracketed) comes from a second,
-untimed pass of the same steps.  `cpu_baseline` times the CPU oracle on a
-bounded row sample of the same step.
+whole step (2*M*N*K per GEMM), from the wall clock around the timed steps.
+`fused_linear` is the w8a8_linear call of step 1 (its TOPS and fraction of
+the 5.0 POP/s dense int8 matrix peak), from a HIP event pair around the call
+in every timed step.  `roofline` reports the up-proj GEMM kernel alone: a
+second timed loop runs the same steps with step 1's two kernels issued
+through their own entry points (w8a8_quantize_act, w8a8_gemm_dequant: the
+same kernels w8a8_linear enqueues), with an event pair around the GEMM.
+Events are recorded on the stream the kernels run on.  The timed loops record
+only those pairs (each recorded event costs a step ~1-3 us), so `kernels_ms`
+(every kernel bracketed) comes from a third, untimed pass.  `cpu_baseline`
+times the CPU oracle on a bounded row sample of the same step.
 """
 from __future__ import annotations
 
@@ -60,9 +63,6 @@ def parse():
     ap.add_argument("--compare", action="store_true",
                     help="per workload shape: fused INT8 linear vs the 'fake INT8' path "
                          "(quantize, dequantize to bf16, bf16 GEMM) vs a plain bf16 GEMM")
-    ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="matrix-core rate on the up-proj's own int8 / e4m3 codes with no memory "
-                         "traffic (the power-limited ceiling), next to the GEMM on the same codes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of known size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -335,6 +335,21 @@ def _time_calls(torch, fn, n_iter, n_copy):
     return ts[len(ts) // 2], ts[0]
 
 
+def fake_int8_forward(w8, x, wq, sw, bias, operands=False):
+    """The "fake INT8" forward the pages start from (Abstract; news write-up,
+    second paragraph): the same per-token int8 quantization of x, then the
+    activation and weight codes dequantized to bf16 (code * scale in fp32,
+    rounded to bf16) and a bf16 GEMM through torch (hipBLASLt), bias added by
+    the GEMM.  With `operands`, also returns the two dequantized matrices."""
+    import torch
+    import torch.nn.functional as F
+    q, sx = w8.w8a8_quantize_act(x)
+    xd = (q.float() * sx[:, None]).to(torch.bfloat16)
+    wd = (wq.float() * sw[:, None]).to(torch.bfloat16)
+    y = F.linear(xd, wd, bias)
+    return (y, xd, wd) if operands else y
+
+
 def compare(args, torch, w8, synthetic):
     """The pages' per-GEMM comparison on MI355X.  For each workload shape, from
     the same bf16 activations, int8 weights + per-channel scales and bf16 bias:
@@ -371,10 +386,7 @@ def compare(args, torch, w8, synthetic):
             w8.w8a8_linear_fp8(x, wf8[i][0], wf8[i][1], b, out=y, workspace=ws)
 
         def fake(i):
-            q, sx = w8.w8a8_quantize_act(x)
-            xd = (q.float() * sx[:, None]).to(torch.bfloat16)
-            wd = (w8s[i][0].float() * w8s[i][1][:, None]).to(torch.bfloat16)
-            return F.linear(xd, wd, b)
+            return fake_int8_forward(w8, x, w8s[i][0], w8s[i][1], b)
 
         def bf16(i):
             return F.linear(x, wbs[i], b)
@@ -396,94 +408,6 @@ def compare(args, torch, w8, synthetic):
                           "speedup_vs_bf16": round(tb[0] / t8[0], 2),
                           "cos_int8_vs_fake": round(cos, 6)}), flush=True)
         del w8s, wf8, wbs, ws, y, x, wq, sw, wq8, sw8, wb
-
-
-def mfma_ceiling(args, torch, w8, synthetic):
-    """Matrix-core throughput on the up-proj's own codes with nothing else
-    running (csrc/mfma_ceiling.hip, built into libw8a8_probe.so), and the clock
-    it runs at, next to the up-proj GEMM on the same codes.  Each probe launch
-    does the up-proj GEMM's share of work per CU (4 waves x 144 iterations x
-    2^21 operations = 1.21 GOP per CU); the codes are the first bytes of the
-    GEMM's weight codes (MFMA "A") and per-token activation codes ("B").
-    The clock falls over the first few milliseconds of sustained load, so every
-    case runs back to back for about as long as the headline bench (150
-    launches): "burst" is the median of launches 1-20, "sustained" of the last
-    50."""
-    import ctypes
-
-    dev = "cuda:0"
-    lib = ctypes.CDLL(os.path.join(ROOT, "w8a8_int8_quantized_quantize_amd", "libw8a8_probe.so"))
-    P = ctypes.c_void_p
-    lib.w8a8_probe_mfma_ceiling.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int,
-                                            ctypes.c_int, P, P, P]
-    lib.w8a8_probe_mfma_ceiling.restype = ctypes.c_int
-    lib.w8a8_probe_mfma_ops.argtypes = [ctypes.c_int, ctypes.c_int]
-    lib.w8a8_probe_mfma_ops.restype = ctypes.c_double
-    grid = torch.cuda.get_device_properties(0).multi_processor_count
-    iters = 144
-    need = grid * 256 * 8 * 16
-    s = synthetic.CONFIGS["dit1024_mlp"][0]
-    st = synthetic.streams(0, s.config_id, s.layer_id)
-    x = synthetic.activations_bf16(st, s.M, s.K, s.outlier_frac).to(dev)
-    w = torch.from_numpy(synthetic.weights_f32(st, s.N, s.K)).to(dev)
-    b = synthetic.bias_bf16(st, s.N).to(dev)
-    q, sx = w8.w8a8_quantize_act(x)
-    wq, sw = w8.w8a8_quantize_weight(w)
-    qf, sxf = w8.w8a8_quantize_act_fp8(x)
-    wqf, swf = w8.w8a8_quantize_weight_fp8(w)
-    del w
-    flat = lambda t: t.view(torch.uint8).reshape(-1)[:need].contiguous()
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(0)
-    uni = lambda: torch.randint(-127, 128, (need,), dtype=torch.int8, device=dev, generator=gen).view(torch.uint8)
-    zero = torch.zeros(need, dtype=torch.uint8, device=dev)
-    cases = [
-        ("int8 32x32x32, workload codes", 0, flat(wq), flat(q)),
-        ("int8 16x16x64, workload codes", 1, flat(wq), flat(q)),
-        ("int8 32x32x32 + LDS fragment reads, workload codes", 2, flat(wq), flat(q)),
-        ("int8 16x16x64 + LDS fragment reads, workload codes", 4, flat(wq), flat(q)),
-        ("fp8 e4m3 32x32x64, workload codes", 3, flat(wqf), flat(qf)),
-        ("int8 32x32x32, uniform random codes", 0, uni(), uni()),
-        ("int8 16x16x64, uniform random codes", 1, uni(), uni()),
-        ("int8 32x32x32, all zero", 0, zero, zero),
-        ("int8 16x16x64, all zero", 1, zero, zero),
-    ]
-    sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
-    stamps = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    ops = lib.w8a8_probe_mfma_ops(grid, iters)
-    res = {}
-    for name, mode, a, bb in cases:
-        def launch(_i=0):
-            rc = lib.w8a8_probe_mfma_ceiling(mode, a.data_ptr(), bb.data_ptr(), need, grid, iters,
-                                             sink.data_ptr(), stamps.data_ptr(), stream)
-            if rc != 0:
-                raise RuntimeError(f"w8a8_probe_mfma_ceiling returned {rc}")
-        ts = _call_times(torch, launch, 150, 1)
-        t = stamps.view(grid, 2).cpu().double()  # the last launch's clock
-        ghz = float((t[:, 0] / (t[:, 1] * 10.0)).mean())
-        burst, sus = _median(ts[:20]), _median(ts[-50:])
-        tops = ops / (sus * 1e-6) / 1e12
-        res[name] = tops
-        print(json.dumps({"mfma_ceiling": name, "us_burst": round(burst, 2), "us_sustained": round(sus, 2),
-                          "TOPS_burst": round(ops / (burst * 1e-6) / 1e12, 1), "TOPS": round(tops, 1),
-                          "frac_of_spec": round(tops / PEAK_INT8_TOPS, 3), "clock_GHz": round(ghz, 3),
-                          "issue_frac_at_clock": round(tops * 1e12 / (grid * 8192 * ghz * 1e9), 3)}),
-              flush=True)
-    # the GEMM itself on the same codes, weights rotated past the last-level cache
-    ncopy = max(1, min(64, -(-600_000_000 // (s.N * s.K))))
-    wqs = [wq] + [wq.clone() for _ in range(ncopy - 1)]
-    y = torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)
-    ts = _call_times(torch, lambda i: w8.w8a8_gemm_dequant(q, sx, wqs[i], sw, b, out=y), 100, ncopy)
-    burst, sus = _median(ts[:20]), _median(ts[-50:])
-    ops = 2.0 * s.M * s.N * s.K
-    tops = ops / (sus * 1e-6) / 1e12
-    cfg = w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(s.M, s.N, s.K))
-    print(json.dumps({"gemm": s.name, "config": cfg, "us_burst": round(burst, 2), "us_sustained": round(sus, 2),
-                      "TOPS_burst": round(ops / (burst * 1e-6) / 1e12, 1), "TOPS": round(tops, 1),
-                      "frac_of_spec": round(tops / PEAK_INT8_TOPS, 3),
-                      "frac_of_ceiling": {k: round(tops / v, 3) for k, v in res.items()
-                                          if "workload" in k and "fp8" not in k}}), flush=True)
 
 
 def main():
@@ -515,35 +439,45 @@ def main():
     if args.compare:
         compare(args, torch, w8, synthetic)
         return 0
-    if args.mfma_ceiling:
-        mfma_ceiling(args, torch, w8, synthetic)
-        return 0
 
     up, down, inp = make_inputs(torch, w8, synthetic, args.rotate, args.fp8)
     stream = torch.cuda.current_stream()
     if args.fp8:
-        quantize, gemm, gelu_quantize = (w8.w8a8_quantize_act_fp8, w8.w8a8_gemm_dequant_fp8,
-                                         w8.w8a8_gelu_quantize_act_fp8)
+        quantize, gemm, gelu_quantize, linear = (w8.w8a8_quantize_act_fp8, w8.w8a8_gemm_dequant_fp8,
+                                                 w8.w8a8_gelu_quantize_act_fp8, w8.w8a8_linear_fp8)
     else:
-        quantize, gemm, gelu_quantize = (w8.w8a8_quantize_act, w8.w8a8_gemm_dequant,
-                                         w8.w8a8_gelu_quantize_act)
+        quantize, gemm, gelu_quantize, linear = (w8.w8a8_quantize_act, w8.w8a8_gemm_dequant,
+                                                 w8.w8a8_gelu_quantize_act, w8.w8a8_linear)
+    ws = torch.empty((w8.w8a8_linear_workspace_bytes(up.M, up.K),), dtype=torch.uint8, device="cuda:0")
+    ws_codes = ws[:up.M * up.K].view(inp["q_x"].dtype).view(up.M, up.K)
 
-    # ev: 5 events bracketing every kernel; ev_up: 2 around the up-proj GEMM
-    def step(i, ev=None, ev_up=None):
+    # One step.  fused=True: the up-projection through the fused entry
+    # w8a8_linear (quantize into the workspace + GEMM), an event pair around
+    # the call (ev_lin).  fused=False: the same two kernels through their own
+    # entry points, so that an event pair (ev_up) brackets the GEMM kernel
+    # alone.  ev: 5 events around every kernel (breakdown pass only).
+    def step(i, fused, ev=None, ev_up=None, ev_lin=None):
         wu, su = inp["w_up"][i % len(inp["w_up"])]
         wd, sd = inp["w_down"][i % len(inp["w_down"])]
-        if ev is not None:
-            ev[0].record(stream)
-        quantize(inp["x_up"], inp["q_x"], inp["s_x"])
-        if ev is not None:
-            ev[1].record(stream)
-        if ev_up is not None:
-            ev_up[0].record(stream)
-        gemm(inp["q_x"], inp["s_x"], wu, su, inp["b_up"], out=inp["y_up"])
-        if ev_up is not None:
-            ev_up[1].record(stream)
-        if ev is not None:
-            ev[2].record(stream)
+        if fused:
+            if ev_lin is not None:
+                ev_lin[0].record(stream)
+            linear(inp["x_up"], wu, su, inp["b_up"], out=inp["y_up"], workspace=ws)
+            if ev_lin is not None:
+                ev_lin[1].record(stream)
+        else:
+            if ev is not None:
+                ev[0].record(stream)
+            quantize(inp["x_up"], inp["q_x"], inp["s_x"])
+            if ev is not None:
+                ev[1].record(stream)
+            if ev_up is not None:
+                ev_up[0].record(stream)
+            gemm(inp["q_x"], inp["s_x"], wu, su, inp["b_up"], out=inp["y_up"])
+            if ev_up is not None:
+                ev_up[1].record(stream)
+            if ev is not None:
+                ev[2].record(stream)
         gelu_quantize(inp["y_up"], inp["q_h"], inp["s_h"])
         if ev is not None:
             ev[3].record(stream)
@@ -551,22 +485,39 @@ def main():
         if ev is not None:
             ev[4].record(stream)
 
+    def pairs(n):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+
     for i in range(args.warmup):
-        step(i)
-    up_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        step(i, True)
+    # timed region 1: the step through the fused entry (value, ms_per_step)
+    lin_events = pairs(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, ev_up=up_events[i])
+        step(i, True, ev_lin=lin_events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # timed region 2: the same step with the up-projection's two kernels
+    # issued through their own entry points, the GEMM kernel event-timed
+    up_events = pairs(args.steps)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, False, ev_up=up_events[i])
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
     # per-kernel breakdown: the same steps again, every kernel bracketed (untimed)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
-        step(i, events[i])
+        step(i, False, events[i])
     torch.cuda.synchronize()
+    # the fused entry wrote the same codes and scales as the split one
+    assert torch.equal(ws_codes, inp["q_x"]), "fused and split up-projection disagree"
 
     ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step_split = (t3 - t2) * 1e3 / args.steps
+    lin_ms = sum(ev[0].elapsed_time(ev[1]) for ev in lin_events) / args.steps
     up_ms = sum(ev[0].elapsed_time(ev[1]) for ev in up_events) / args.steps
     seg = [[ev[j].elapsed_time(ev[j + 1]) for ev in events] for j in range(4)]
     avg = [sum(s) / len(s) for s in seg]
@@ -574,6 +525,7 @@ def main():
     ops_down = 2.0 * down.M * down.N * down.K
     value = (ops_up + ops_down) / (ms_step * 1e-3) / 1e12
     gemm_up_tops = ops_up / (up_ms * 1e-3) / 1e12
+    lin_tops = ops_up / (lin_ms * 1e-3) / 1e12
     gemm_down_tops = ops_down / (avg[3] * 1e-3) / 1e12
     q_bytes = 3.0 * up.M * up.K + 4 * up.M
     g_bytes = 3.0 * down.M * down.K + 4 * down.M
@@ -599,9 +551,15 @@ def main():
                      "traffic": traffic_entry(),
                      "kernel": "gemm_kernel, up-proj M=4096 K=3072 N=12288 (int8 ops per launch "
                                "2*M*N*K / mean HIP-event duration)"},
-        # the up-proj GEMM in the timed steps (the roofline's figure), and every
-        # kernel in the untimed pass with all kernels bracketed
+        # the fused entry w8a8_linear at the headline shape (quantize + GEMM +
+        # epilogue, one call), event-timed in every step of timed region 1
+        "fused_linear": {"entry": "w8a8_linear", "M": up.M, "K": up.K, "N": up.N,
+                         "us": round(lin_ms * 1e3, 2), "TOPS": round(lin_tops, 1),
+                         "frac": round(lin_tops / PEAK_INT8_TOPS, 4)},
+        # the up-proj GEMM kernel in timed region 2 (the roofline's figure), and
+        # every kernel in the untimed pass with all kernels bracketed
         "gemm_up_ms_timed": round(up_ms, 4),
+        "ms_per_step_split_entries": round(ms_step_split, 4),
         "kernels_ms": {"quantize_x": round(avg[0], 4), "gemm_up": round(avg[1], 4),
                        "gelu_quantize": round(avg[2], 4), "gemm_down": round(avg[3], 4)},
         "per_kernel": {

@@ -22,7 +22,8 @@
  *
  * Conventions for every entry point below:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing and keeps no mutable state; calls are thread-safe.
+ *     allocates nothing; its only mutable state is a per-device cache of
+ *     kernel occupancy figures, filled on first use (calls are thread-safe).
  *   - Matrices are row-major with the reduction dimension K contiguous.
  *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
  *     Work is enqueued asynchronously on it; the return value covers argument
@@ -115,7 +116,8 @@ int w8a8_gemm_dequant(const int8_t* q_x, const float* s_x, const int8_t* w_q,
                       int64_t K, void* y_bf16, void* stream);
 
 /* Bytes of device workspace w8a8_linear needs: the int8 codes [M, K] and the
- * fp32 scales [M] of the activations, each padded to 256 bytes. */
+ * fp32 scales [M] of the activations, each padded to 256 bytes.  0 when
+ * M <= 0 or K < 0; SIZE_MAX when the size does not fit in size_t. */
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
 
 /*

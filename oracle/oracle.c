@@ -225,14 +225,30 @@ void oracle_quantize_rows_bf16_fp8(const uint16_t* x, int64_t rows, int64_t K, i
   }
 }
 
-/* acc[m][n] = sum_k decode(a[m][k]) * decode(b[n][k]), exact in fp64 (see header). */
+/* acc[m][n] = sum_k decode(a[m][k]) * decode(b[n][k]), exact in fp64 (see header).
+ * Each output is summed over k = 0, 1, ... from 0.0, as written; the codes go
+ * through a 256-entry table of e4m3_decode's values (the decode depends on the
+ * byte alone), and eight outputs of a row advance together, which only
+ * interleaves independent sums. */
 void oracle_gemm_fp8(const uint8_t* a, int64_t lda, const uint8_t* b, int64_t ldb, int64_t M,
                      int64_t N, int64_t K, double* acc) {
+  double val[256];
+  for (int c = 0; c < 256; ++c) val[c] = e4m3_decode((uint8_t)c);
 #pragma omp parallel for schedule(static)
   for (int64_t m = 0; m < M; ++m) {
-    for (int64_t n = 0; n < N; ++n) {
+    const uint8_t* ar = a + m * lda;
+    int64_t n = 0;
+    for (; n + 8 <= N; n += 8) {
+      double sum[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+      for (int64_t k = 0; k < K; ++k) {
+        const double x = val[ar[k]];
+        for (int j = 0; j < 8; ++j) sum[j] += x * val[b[(n + j) * ldb + k]];
+      }
+      for (int j = 0; j < 8; ++j) acc[m * N + n + j] = sum[j];
+    }
+    for (; n < N; ++n) {
       double sum = 0.0;
-      for (int64_t k = 0; k < K; ++k) sum += e4m3_decode(a[m * lda + k]) * e4m3_decode(b[n * ldb + k]);
+      for (int64_t k = 0; k < K; ++k) sum += val[ar[k]] * val[b[n * ldb + k]];
       acc[m * N + n] = sum;
     }
   }

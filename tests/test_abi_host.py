@@ -169,25 +169,3 @@ def test_module_swap_host_checks():
     assert w8.quantize_linears(odd) == 0
     assert w8.quantize_linears(cpu, include=lambda name, lin: False) == 0
     assert isinstance(cpu[0], torch.nn.Linear)
-
-
-def test_probe_library_host_checks():
-    """The measurement probe (bench.py --mfma-ceiling) is a library of its own:
-    it loads, exports its two entry points, counts the operations of a launch,
-    and rejects bad arguments before any launch."""
-    import os
-    path = os.path.join(os.path.dirname(w8.library_path()), "libw8a8_probe.so")
-    pl = ctypes.CDLL(path)
-    pl.w8a8_probe_mfma_ops.argtypes = [ctypes.c_int, ctypes.c_int]
-    pl.w8a8_probe_mfma_ops.restype = ctypes.c_double
-    f = pl.w8a8_probe_mfma_ceiling
-    f.argtypes = [ctypes.c_int, P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, P]
-    f.restype = ctypes.c_int
-    # 256 workgroups x 4 waves x 144 iterations x 2^21 operations
-    assert pl.w8a8_probe_mfma_ops(256, 144) == 256 * 4 * 144 * 2.0 ** 21
-    need = 256 * 256 * 8 * 16
-    assert f(0, None, A, need, 256, 144, A, A, None) == -1           # null operand
-    assert f(5, A, A, need, 256, 144, A, A, None) == -1              # unknown mode
-    assert f(0, A, A, need - 16, 256, 144, A, A, None) == -1         # buffers too small
-    assert f(4, A, A, need, 256, 143, A, A, None) == -1              # odd iterations, mode 4
-    assert f(1, A, A, need, 0, 144, A, A, None) == -1                # empty grid

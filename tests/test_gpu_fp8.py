@@ -3,13 +3,19 @@
 Quantization (codes and scales) is deterministic and compared bit for bit.
 The GEMM accumulates e4m3 products on the matrix cores in fp32 with rounding
 of their own, so its bf16 output is compared with the oracle's (built on the
-exact sum of products) within a derived bound:
+exact sum of products) within a bound:
     |y_gpu - y_exact| <= |s_x s_w| * 2^-12 * sum_k |a_k b_k|  +  1 bf16 ulp of y,
-where 2^-12 covers the matrix cores' accumulation error (measured on this
-hardware at up to 2^-13.5 of sum |a_k b_k| for one 64-deep product, with
-fp32 additions across steps adding at most K/64 * 2^-24 relative) and the
-ulp covers the final rounding.  Cosine >= 0.99999 against the oracle and no
-NaN/Inf are required as well.
+where the ulp covers the final rounding and 2^-12 the matrix cores'
+accumulation error.  That constant is a CALIBRATION, not a derivation: the
+rounding inside one v_mfma_scale_f32_*_f8f6f4 product is not specified in a
+form this test could derive a bound from, so
+test_fp8_accumulation_error_calibration measures it on the GPU (the error of
+single 64-deep products and of K = 3072 sums, resolved on outputs whose exact
+sum nearly cancels) and asserts it stays within 2^-12; it prints the worst
+case it saw (up to 2^-13.5 of sum |a_k b_k| when the constant was set).  FP8
+GEMM parity therefore rests on that calibration.  fp32 additions across
+64-deep steps add at most K/64 * 2^-24 relative.  Cosine >= 0.99999 against
+the oracle and no NaN/Inf are required as well.
 """
 from __future__ import annotations
 
@@ -20,7 +26,7 @@ import torch
 import oracle
 import synthetic
 import w8a8_int8_quantized_quantize_amd as w8
-from gpu_helpers import DEV, bits, cosine, dev_bf16, host, sample_rows
+from gpu_helpers import DEV, bits, cosine, dev_bf16, host
 
 pytestmark = pytest.mark.gpu
 
@@ -125,13 +131,16 @@ def test_gemm_fp8_every_config_within_bound(M, N, K, with_bias):
     assert_fp8_gemm_bound(y, qx, sx, qw, sw, bb, f"linear {M}x{N}x{K}")
 
 
-# More interior tiles than persistent workgroups (M = 4096, N = 4352: 272 to
-# 1088 interior tiles by configuration): workgroups run several tiles in a
-# row, with K from one LDS stage to several.
-@pytest.mark.parametrize("K", [64, 128, 256, 384])
-def test_gemm_fp8_consecutive_interior_tiles_every_config(K):
-    M, N = 4096, 4352
-    rng = np.random.default_rng(7 * K)
+# More interior tiles than persistent workgroups, so workgroups run several
+# tiles in a row: M = 4096, N = 4352 (272 to 1088 interior tiles by
+# configuration) with K from one LDS stage to several, and the up-projection's
+# M = 4096, N = 12288 at K = 384, 640 and 3072, where a workgroup's later tiles
+# run the K-loop waits that let the previous tile's stores stay in flight.
+@pytest.mark.parametrize("M,N,K", [(4096, 4352, 64), (4096, 4352, 128), (4096, 4352, 256),
+                                   (4096, 4352, 384), (4096, 12288, 384), (4096, 12288, 640),
+                                   (4096, 12288, 3072)])
+def test_gemm_fp8_consecutive_interior_tiles_every_config(M, N, K):
+    rng = np.random.default_rng(7 * K + N)
     xb = rand_bits(rng, M, K, outliers=1)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     bb = rand_bits(rng, 1, N, scale=0.1)[0]
@@ -170,7 +179,8 @@ def test_gemm_fp8_extremes_and_k_zero():
 
 @pytest.mark.parametrize("shape", [s for s in synthetic.CONFIGS["dit1024_mlp"]] +
                          [synthetic.CONFIGS["dit768_attn"][1]], ids=lambda s: s.name)
-def test_full_size_linear_fp8_sampled(shape):
+def test_full_size_linear_fp8(shape):
+    # whole output at full size, in the configuration the library selects
     st = synthetic.streams(0, shape.config_id, shape.layer_id)
     x = synthetic.activations_bf16(st, shape.M, shape.K, shape.outlier_frac)
     w = synthetic.weights_f32(st, shape.N, shape.K)
@@ -179,11 +189,12 @@ def test_full_size_linear_fp8_sampled(shape):
     qw, sw = oracle.quantize_rows_f32_fp8(w)
     assert np.array_equal(host(dwq), qw) and np.array_equal(host(dsw), sw)
     y = w8.w8a8_linear_fp8(x.to(DEV), dwq, dsw, b.to(DEV))
-    rows = sample_rows(shape.M, 16)
-    xb = synthetic.bf16_bits(x)[rows]
+    xb = synthetic.bf16_bits(x)
     bb = synthetic.bf16_bits(b)
     qx, sx = oracle.quantize_rows_bf16_fp8(xb)
-    assert_fp8_gemm_bound(bits(y)[rows], qx, sx, qw, sw, bb, shape.name)
+    dq, dsx = w8.w8a8_quantize_act_fp8(x.to(DEV))
+    assert np.array_equal(host(dq), qx) and np.array_equal(host(dsx), sx)
+    assert_fp8_gemm_bound(bits(y), qx, sx, qw, sw, bb, shape.name)
 
 
 @pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (4, 48), (4133, 3072),
@@ -197,3 +208,40 @@ def test_gelu_quantize_fp8_teacher_forced(M, K):
     assert np.array_equal(host(s), so) and np.array_equal(host(q), qo)
     q2, s2, _ = w8.w8a8_gelu_quantize_act_fp8(dev_bf16(yb))
     assert torch.equal(q2, q) and torch.equal(s2, s)
+
+
+@pytest.mark.parametrize("K", [64, 3072])
+def test_fp8_accumulation_error_calibration(K):
+    """Measures the matrix cores' fp8 accumulation error against the exact sum
+    and checks it against EPS_ACC (the calibration the FP8 bound rests on).
+    Unit scales and no bias make y = bf16(acc) exactly, so the accumulator's
+    error is at least |y - exact| - ulp(y)/2; on outputs whose exact sum
+    cancels to below 2^-6 of sum |a_k b_k| that half ulp is below
+    2^-15 sum |a_k b_k|, fine enough to resolve the error being measured.
+    Codes: the workload's distributions (per-token codes of N(0,1)
+    activations with outlier columns, per-channel codes of N(0,0.02)
+    weights)."""
+    M = N = 2048
+    rng = np.random.default_rng(1000 + K)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    qx, _ = oracle.quantize_rows_bf16_fp8(xb)
+    qw, _ = oracle.quantize_rows_f32_fp8(w)
+    ones_m = torch.ones((M,), dtype=torch.float32, device=DEV)
+    ones_n = torch.ones((N,), dtype=torch.float32, device=DEV)
+    exact, mag = fp8_exact_sums(qx, qw)
+    worst = {}
+    for c in range(w8.w8a8_gemm_fp8_num_configs()):
+        y = bf16_vals(bits(w8.w8a8_gemm_dequant_fp8(torch.from_numpy(qx).to(DEV), ones_m,
+                                                    torch.from_numpy(qw).to(DEV), ones_n, config=c)))
+        assert np.all(np.isfinite(y))
+        half_ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(y), 1e-30))[1] - 9)  # ulp(y) / 2
+        err_lo = np.maximum(np.abs(y - exact) - half_ulp, 0.0) / np.maximum(mag, 1e-30)
+        sharp = np.abs(exact) < mag * 2.0 ** -6
+        assert sharp.sum() > 1000
+        worst[w8.w8a8_gemm_fp8_config_name(c)] = float(err_lo[sharp].max())
+        assert err_lo.max() <= EPS_ACC, (c, float(err_lo.max()))
+    print(f"\nfp8 accumulation error, K={K}: worst lower bound over sharp outputs, "
+          f"in units of sum|ab|: " + ", ".join(f"{k} 2^{np.log2(max(v, 2.0 ** -60)):.2f}"
+                                            for k, v in worst.items()))
+

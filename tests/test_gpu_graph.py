@@ -98,3 +98,40 @@ def test_graph_replay_fp8_linear():
     from test_gpu_fp8 import assert_fp8_gemm_bound
     qx, sx = oracle.quantize_rows_bf16_fp8(bits(x))
     assert_fp8_gemm_bound(bits(got), qx, sx, host(wq), host(sw), None, "graph fp8")
+
+
+def test_module_graph_replay_after_larger_eager_calls():
+    """W8A8Linear captured in a graph: its per-call workspace comes from the
+    graph's memory pool, so eager calls with more tokens between replays
+    (which take larger workspaces from the ordinary pool) cannot disturb the
+    captured one.  Every replay equals the eager result on the same input."""
+    rng = np.random.default_rng(91)
+    M, N, K = 257, 1536, 3072
+    w = torch.from_numpy((rng.standard_normal((N, K)) * 0.02).astype(np.float32)).to(DEV)
+    b = torch.from_numpy((rng.standard_normal(N) * 0.1).astype(np.float32)).to(DEV)
+    lin = w8.W8A8Linear.from_float(w, b)
+    x = dev_bf16(rand_bf16_bits(rng, M, K))
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lin(x)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y = lin(x)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        big = dev_bf16(rand_bf16_bits(rng, 4 * M + rep, K))
+        yb = lin(big)                       # eager, more tokens, own workspace
+        x.copy_(dev_bf16(rand_bf16_bits(rng, M, K)))
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        want = lin(x)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), rep
+        wq, sw = host(lin.w_q), host(lin.s_w)
+        rows = np.arange(0, 4 * M + rep, 97)
+        ref = oracle.linear(bits(big)[rows], wq, sw, bits(lin.bias))
+        assert np.array_equal(bits(yb)[rows], ref["y"]), rep

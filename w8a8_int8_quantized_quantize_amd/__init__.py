@@ -444,7 +444,6 @@ class W8A8Linear(torch.nn.Module):
         self.register_buffer("w_q", w_q)
         self.register_buffer("s_w", s_w)
         self.register_buffer("bias", bias)
-        self._ws = None
 
     @classmethod
     def from_float(cls, weight: torch.Tensor, bias: torch.Tensor | None = None,
@@ -466,11 +465,11 @@ class W8A8Linear(torch.nn.Module):
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
-        need = w8a8_linear_workspace_bytes(x2.shape[0], x2.shape[1])
-        if self._ws is None or self._ws.numel() < need or self._ws.device != x2.device:
-            self._ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x2.device)
+        # the workspace (activation codes + scales) is taken from torch's
+        # caching allocator for each call, like any temporary: it is then
+        # stream- and graph-pool-aware, and no layer holds memory between calls
         fn = w8a8_linear_fp8 if self.fp8 else w8a8_linear
-        y = fn(x2, self.w_q, self.s_w, self.bias, workspace=self._ws)
+        y = fn(x2, self.w_q, self.s_w, self.bias)
         return y.reshape(*lead, self.out_features)
 
 

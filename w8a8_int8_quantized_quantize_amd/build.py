@@ -27,9 +27,6 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
-# measurement probe (bench.py --mfma-ceiling), a library of its own
-PROBE_SOURCE = "mfma_ceiling.hip"
-PROBE_LIB = os.path.join(PKG, "libw8a8_probe.so")
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -64,14 +61,13 @@ def build(save_temps: bool | None = None) -> str:
     if r.returncode != 0:
         raise RuntimeError("gen_gelu_lut.py failed:\n" + r.stderr)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
-        objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES + [PROBE_SOURCE]))
-    for lib, parts in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
-        tmp = lib + ".tmp%d" % os.getpid()
-        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + parts
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            raise RuntimeError("link failed:\n" + r.stderr)
-        os.replace(tmp, lib)
+        objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, LIB)
     return LIB
 
 

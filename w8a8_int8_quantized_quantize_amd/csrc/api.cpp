@@ -177,7 +177,11 @@ int w8a8_gemm_ex(const int8_t* q_x, const float* s_x, const int8_t* w_q, const f
 
 size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K < 0) return 0;
-  return pad(static_cast<size_t>(M) * static_cast<size_t>(K)) + pad(static_cast<size_t>(M) * 4);
+  // a size that does not fit in size_t is reported as SIZE_MAX, which no
+  // workspace can provide (the fused entry then fails with W8A8_ERR_WORKSPACE)
+  const size_t m = static_cast<size_t>(M), k = static_cast<size_t>(K);
+  if (m > (SIZE_MAX - 2 * kPad) / (k + 4)) return SIZE_MAX;
+  return pad(m * k) + pad(m * 4);
 }
 
 int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w, const void* bias_bf16,

@@ -54,6 +54,8 @@
 // 16 (API contract), so a chunk is entirely inside or outside K.
 #include "internal.h"
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace w8a8 {
@@ -1405,15 +1407,29 @@ constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
 // Persistent grid: as many workgroups of `kernel` as fit on the device at
 // once (a multiple of the 8 XCDs), or one per tile if there are fewer tiles.
-template <class K>
-hipError_t persistent_grid(K kernel, int threads, int64_t tiles, int& grid) {
-  int dev = 0, cus = 0, per_cu = 0;
+// The resident count depends only on the device and the kernel, so it is
+// asked of the runtime once per (kernel, device) and kept: the occupancy
+// query costs microseconds of host time, which the launch-bound small shapes
+// would otherwise pay on every call.  (Racing first calls store the same
+// value.)
+constexpr int kMaxDevices = 64;
+template <auto Kernel>
+hipError_t persistent_grid(int threads, int64_t tiles, int& grid) {
+  static std::atomic<int> cache[kMaxDevices];  // per kernel; 0: not known yet
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
   if (e != hipSuccess) return e;
-  int64_t resident = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : 1);
-  resident = resident >= 8 ? (resident / 8) * 8 : resident;
+  int resident = (dev >= 0 && dev < kMaxDevices) ? cache[dev].load(std::memory_order_relaxed) : 0;
+  if (resident == 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0);
+    if (e != hipSuccess) return e;
+    int64_t r = static_cast<int64_t>(cus) * (per_cu > 0 ? per_cu : 1);
+    r = r >= 8 ? (r / 8) * 8 : r;
+    resident = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(r, INT32_MAX)));
+    if (dev >= 0 && dev < kMaxDevices) cache[dev].store(resident, std::memory_order_relaxed);
+  }
   grid = static_cast<int>(tiles < resident ? tiles : resident);
   return hipSuccess;
 }
@@ -1440,7 +1456,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t E = interior ? (MT > MTi ? NT : 0) + (NT > NTi ? MTi : 0) : MT * NT;
   int grid = 0;
   if (Ti > 0) {
-    hipError_t e = persistent_grid(gemm_kernel<C, I32, false>, C::kThreads, Ti, grid);
+    hipError_t e = persistent_grid<gemm_kernel<C, I32, false>>(C::kThreads, Ti, grid);
     if (e != hipSuccess) return e;
     gemm_kernel<C, I32, false><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
         a, static_cast<int>(Ti), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),
@@ -1449,7 +1465,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (E > 0) {
-    hipError_t e = persistent_grid(gemm_kernel<C, I32, true>, C::kThreads, E, grid);
+    hipError_t e = persistent_grid<gemm_kernel<C, I32, true>>(C::kThreads, E, grid);
     if (e != hipSuccess) return e;
     gemm_kernel<C, I32, true><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
         a, static_cast<int>(E), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),

@@ -343,10 +343,16 @@ __device__ __forceinline__ void stage_lut(uint16_t* lut) {
 // (i = wave + 16 n for its n-th row) issues that row's loads once at least
 // i - depth + 1 of the workgroup's rows have arrived, as counted in LDS.
 // Rows increase with i, so every row before a waiting one exists and is
-// counted once its own (earlier) wait has ended: every wait ends.
+// counted once its own (earlier) wait has ended: every wait ends.  The wait
+// only paces the loads (the row's data and codes do not depend on it), so it
+// also ends after kMaxRowWaits polls (tens of milliseconds), whatever the
+// count: a wave that stopped counting can slow its workgroup, never hang it.
+constexpr int kMaxRowWaits = 1 << 20;
 __device__ __forceinline__ void wait_rows_arrived(const int* arrived, int need) {
-  while (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < need)
+  for (int i = 0; i < kMaxRowWaits; ++i) {
+    if (__hip_atomic_load(arrived, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= need) break;
     __builtin_amdgcn_s_sleep(1);
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
