@@ -58,6 +58,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time every GEMM configuration on every workload shape instead")
     ap.add_argument("--sweep-iters", type=int, default=20)
+    ap.add_argument("--shapes", default="",
+                    help="comma-separated workload shape names for --sweep / --compare (default: all)")
     ap.add_argument("--fp8", action="store_true",
                     help="run the step through the FP8 (e4m3) entry points instead of int8")
     ap.add_argument("--compare", action="store_true",
@@ -238,6 +240,8 @@ def cpu_baseline(up, down, seconds):
 def sweep(args, torch, w8, synthetic):
     dev = "cuda:0"
     shapes = [s for v in synthetic.CONFIGS.values() for s in v]
+    if args.shapes:
+        shapes = [s for s in shapes if s.name in args.shapes.split(",")]
     for s in shapes:
         # the workload's own seeded inputs: the matrix cores draw power in
         # proportion to the bits that toggle, so the code distribution (small
@@ -362,6 +366,8 @@ def compare(args, torch, w8, synthetic):
     import torch.nn.functional as F
     dev = "cuda:0"
     shapes = [s for k, v in synthetic.CONFIGS.items() if k != "unit" for s in v]
+    if args.shapes:
+        shapes = [s for s in shapes if s.name in args.shapes.split(",")]
     for s in shapes:
         st = synthetic.streams(0, s.config_id, s.layer_id)
         x = synthetic.activations_bf16(st, s.M, s.K, s.outlier_frac).to(dev)

@@ -75,12 +75,19 @@ constexpr int kGroupM = 8;  // M-tiles per group in the grouped tile order
 // depends on r & 15 only, so every fragment of a tile shares it and fragment
 // addresses differ by compile-time offsets.  128-byte rows (8 chunks): any 8
 // aligned consecutive rows read at one chunk hit 8 distinct 16-byte bank
-// groups, and any 16 rows hit 16 distinct (row parity, slot) pairs, i.e. no
-// conflict whether a 256-byte bank line holds one or two rows.  64-byte rows
-// (4 chunks): the same for 2 and 4 rows per bank line.
-template <int SLOTS>
+// groups, and any 16 rows hit 16 distinct (row parity, slot) pairs.  64-byte
+// rows (4 chunks), 32x32 operands (lane l: row l % 32, chunk l / 32): the same
+// for 2 and 4 rows per bank line.  64-byte rows read as 16x16x64 operands
+// (lane l: row l % 16, chunk l / 16) take R1 = true, c ^ ((r >> 1) & 3): which
+// lanes the LDS serves together for a 16-byte read is not documented, and
+// measured on gfx950 (SQ_LDS_BANK_CONFLICT of one wave reading each layout,
+// a probe outside this library) the 64-byte-row form above costs that read 4
+// conflict cycles (8 LDS cycles instead of 4) whatever the chunk order,
+// while this one costs none.
+template <int SLOTS, bool R1 = false>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (SLOTS == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
+  else if constexpr (R1) return c ^ ((r >> 1) & 3);
   else return c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1));
 }
 
@@ -131,19 +138,16 @@ struct Mfma<32, true> {
 // Which 16-byte chunk of a k-step piece h of a lane holds, for lane group
 // q = lane / MF.  The K positions inside one MFMA are summed in any order, so
 // the lane -> chunk assignment is free as long as both operands use the same
-// one.  It is chosen for the LDS: the reads of lanes l and l + 32 are served
-// together, and they must fall in different banks.  With the natural order
-// they read chunks two apart for the 16x16x64 operands (q = 0 / 2) and for the
-// first pieces of the FP8 32-byte operands, which the swizzle maps to the
-// same banks (measured: SQ_LDS_BANK_CONFLICT 4 cycles per fragment read).
-// Adjacent chunks, as the 32x32x32 int8 operands read them, never conflict:
-//   int8 32x32x32: q                       (lanes l, l + 32: chunks c, c + 1)
-//   int8 16x16x64: q = 0, 1, 2, 3 -> 0, 2, 1, 3
-//   FP8 32x32x64:  pieces q and q + 2      (lanes l, l + 32: c, c + 1 and c + 2, c + 3)
-template <int MF, bool FP8>
+// one; it is chosen with the LDS swizzle (see swz) so that fragment reads are
+// free of bank conflicts:
+//   int8 32x32x32: q
+//   int8 16x16x64, 64-byte rows (swizzle R1): q
+//   int8 16x16x64, 128-byte rows: q = 0, 1, 2, 3 -> 0, 2, 1, 3
+//   FP8 32x32x64:  pieces q and q + 2
+template <int MF, bool FP8, bool R1 = false>
 __device__ __forceinline__ int piece_chunk(int q, int h) {
   if constexpr (FP8) return q + 2 * h;
-  else if constexpr (MF == 16) return ((q & 1) << 1) | (q >> 1);
+  else if constexpr (MF == 16 && !R1) return ((q & 1) << 1) | (q >> 1);
   else return q;
 }
 
@@ -152,6 +156,8 @@ struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = STAGES_;
   static constexpr int MF = MF_;
   static constexpr bool kFp8 = FP8_;
+  // 16x16x64 int8 operands in 64-byte LDS rows take the R1 swizzle (see swz)
+  static constexpr bool kSwzR1 = MF_ == 16 && !FP8_ && BK_ == 64;
   using Op = Mfma<MF, FP8_>;
   using Acc = typename Op::Acc;
   static constexpr int kSlots = BK / 16;            // 16-byte chunks per LDS row
@@ -288,7 +294,7 @@ struct Loader {
     const int lr = lane / C::kSlots, p = lane % C::kSlots;
     // row & 15 of this wave's blocks: (j R) & 15 + lr, j = wave + jj kWaves
     const int rbase = (R == 8) ? ((wave & 1) * 8) : 0;
-    lane_off = static_cast<uint32_t>(lr * K + swz<C::kSlots>(rbase + lr, p) * 16);
+    lane_off = static_cast<uint32_t>(lr * K + swz<C::kSlots, C::kSwzR1>(rbase + lr, p) * 16);
   }
 
 
@@ -333,7 +339,7 @@ struct Loader {
         int64_t row = g0 + lr;
         const int64_t lim = is_w ? N : M;
         if (row > lim - 1) row = lim - 1;
-        int64_t k = k0 + swz<C::kSlots>(row0 + lr, p) * 16;
+        int64_t k = k0 + swz<C::kSlots, C::kSwzR1>(row0 + lr, p) * 16;
         if (k > K - 16) k = K - 16;
         const int8_t* g = op + row * K + k;
         __builtin_amdgcn_global_load_lds(g, d, 16, 0, 0);
@@ -637,7 +643,7 @@ __device__ __forceinline__ void zero_tail(Frags<C>& fr, int64_t kstep0, int64_t 
   const int q = lane / C::MF;
 #pragma unroll
   for (int h = 0; h < RD; ++h)
-    if (kstep0 + 16 * piece_chunk<C::MF, C::kFp8>(q, h) >= K) {  // piece h lies past K
+    if (kstep0 + 16 * piece_chunk<C::MF, C::kFp8, C::kSwzR1>(q, h) >= K) {  // piece h lies past K
 #pragma unroll
       for (int f = 0; f < C::FM; ++f)
 #pragma unroll
@@ -888,7 +894,7 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
       const uint32_t l = static_cast<uint32_t>(
-          fr * C::BK + swz<C::kSlots>(fr, ks * (SB / 16) + piece_chunk<C::MF, C::kFp8>(fq, 0)) * 16);
+          fr * C::BK + swz<C::kSlots, C::kSwzR1>(fr, ks * (SB / 16) + piece_chunk<C::MF, C::kFp8, C::kSwzR1>(fq, 0)) * 16);
       lw[ks] = l + static_cast<uint32_t>(wn * C::TN * C::BK);
       lx[ks] = l + static_cast<uint32_t>(C::BN * C::BK + wm * C::TM * C::BK);
     }
@@ -1172,6 +1178,165 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
   }
 }
 
+// ------------------------------------------------------------ ping-pong --
+// Interior tiles with two waves per SIMD that take turns on the matrix core.
+// The 8 waves form two groups of four (one wave of each group per SIMD):
+// group 0 owns output rows [0, BM/2) of the tile, group 1 rows [BM/2, BM);
+// within a group wave w owns columns [w TN, (w+1) TN).  Every k-step of a
+// wave is a memory phase (its fragments for the step read from LDS into
+// registers, its share of a refill stage issued global -> LDS) followed by
+// a compute phase (the step's MFMAs back to back from registers), and the
+// phases are separated by workgroup barriers.  Group 1 starts one barrier
+// late, so while one group's wave on a SIMD runs its compute phase the other
+// group's wave runs its memory phase: the matrix core is fed by one wave
+// without LDS reads, loads or address arithmetic between its MFMAs (issued
+// from a single wave, those cost the 16x16x64 MFMA stream about a third of
+// its rate).  A tile's epilogue runs in the group's memory slot, alongside
+// the other group's MFMAs.
+//
+// Interval k lies between the k-th and (k+1)-th barrier; group 0 runs the
+// memory phase of step i in interval 2i and its compute phase in 2i + 1,
+// group 1 one interval later.  Hence:
+//  * stage i's buffer is read in intervals 2i (group 0) and 2i + 1 (group
+//    1); the refill issued in step i + 1's memory phase (interval >= 2i + 2)
+//    overwrites it only after every wave passed the barrier that ends 2i + 1
+//    (block_barrier waits for the wave's own LDS reads first);
+//  * stage i + 1 is first read in interval 2i + 2, so every wave waits for
+//    its own loads of that stage before the barrier that opens it: group 0
+//    at the end of its compute phase of step i, group 1 at the end of its
+//    memory phase of step i.
+// Loads and stores of a wave retire in issue order; a wave's loads of stage
+// i + 1 are followed by the refills of S - 2 later steps (L loads each), and
+// for the first S - 2 steps of a tile also by the previous tile's epilogue
+// stores, which fixes each wait count at compile time.  (Waves 0-2 also load
+// the tile's epilogue vectors at step 0, one load each, after those stages:
+// their waits then cover one load more than needed.)  The refills of a
+// tile's last S - 1 steps load the workgroup's next tile's first stages
+// (consecutive tiles chain, so a tile needs K >= S x BK), or repeat the last
+// stage after the workgroup's last tile.  The epilogue vectors (scales, bias)
+// alternate between two LDS buffers from tile to tile: group 0 loads the next
+// tile's while group 1 may still read the previous ones.
+template <class C, bool OUT_I32>
+__global__ __launch_bounds__(C::kThreads) void gemm_pp_kernel(GemmArgs a, int T, int MTi, int NTi) {
+  static_assert(C::kWaves == 8 && C::WM == 2 && C::WN == 4 && C::kSteps == 1 && C::kSpread,
+                "ping-pong tiles: 2 x 4 waves, one k-step per stage, 3+ stages");
+  constexpr int S = C::STAGES;
+  constexpr int L = C::kLoadsPerWave;
+  constexpr bool EPI = !OUT_I32 && C::kEpiLds;
+  constexpr int kStores = OUT_I32 ? C::FM * C::FN * C::Op::kGroups : kFastStores<C>;
+  static_assert((S - 2) * L + kStores <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[S * C::kStage + (EPI ? 2 * C::kEpiBytes : 0)];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int grp = wave / C::WN;  // = wm
+  const int wn = wave % C::WN;
+  int t = blockIdx.x;
+  if (t >= T) return;
+  const int KST = static_cast<int>(a.K / C::BK);  // >= S (host condition)
+  auto origin = [&](int tt, int64_t& m, int64_t& n) {
+    int tm, tn;
+    tile_coords(tt, T, MTi, NTi, tm, tn);
+    m = static_cast<int64_t>(tm) * C::BM;
+    n = static_cast<int64_t>(tn) * C::BN;
+  };
+  int64_t m0, n0;
+  origin(t, m0, n0);
+  // fragment addresses: row MF f + lane % MF of the wave's tile, chunk
+  // piece_chunk(lane / MF) of the 64-byte k-step
+  uint32_t lw, lx;
+  {
+    const int fr = lane % C::MF, fq = lane / C::MF;
+    const uint32_t l = static_cast<uint32_t>(fr * C::BK + swz<C::kSlots, C::kSwzR1>(fr, piece_chunk<C::MF, false, C::kSwzR1>(fq, 0)) * 16);
+    lw = l + static_cast<uint32_t>(wn * C::TN * C::BK);
+    lx = l + static_cast<uint32_t>(C::BN * C::BK + grp * C::TM * C::BK);
+  }
+  {
+    Loader<C, true> ld(a, n0, m0, wave, lane);
+#pragma unroll
+    for (int s = 0; s < S - 1; ++s) ld.template issue_part_at<0, L>(n0, m0, s, smem + s * C::kStage, wave, lane);
+  }
+  wait_vm<(S - 2) * L>();  // this wave's stage 0
+  block_barrier();         // everyone's
+  if (grp == 1) block_barrier();  // group 1 runs one interval behind
+  int ph = 0;        // LDS buffer of the current tile's stage 0
+  int par = 0;       // epilogue-vector buffer of the current tile
+  bool stored = false;
+  typename C::Acc acc[C::FN][C::FM];
+  Frags<C> f;
+  for (;;) {
+    const int tnext = t + static_cast<int>(gridDim.x);
+    const bool more = tnext < T;
+    int64_t m1 = m0, n1 = n0;
+    if (more) origin(tnext, m1, n1);
+    int ln = lane, wv = wave;
+    asm volatile("" : "+v"(ln), "+s"(wv));
+    Loader<C, true> ld(a, n0, m0, wv, ln);
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) acc[i][j] = typename C::Acc{};
+    int8_t* epi = smem + par * C::kEpiBytes;  // epilogue vectors at epi + kEpiOffset
+    for (int i = 0; i < KST; ++i) {
+      // ---- memory phase of step i
+      sched_fence();
+      const int8_t* cur = smem + ((ph + i) % S) * C::kStage;
+#pragma unroll
+      for (int q = 0; q < C::FM; ++q) f.x[q] = load_frag<C>(cur, lx + q * C::MF * C::BK);
+#pragma unroll
+      for (int q = 0; q < C::FN; ++q) f.w[q] = load_frag<C>(cur, lw + q * C::MF * C::BK);
+      if constexpr (EPI) {
+        if (i == 0 && grp == 0) stage_epilogue_vectors<C>(a, epi, m0, n0, wv, ln);
+      }
+      {
+        const int rs = i + S - 1;  // refill: stage rs, into the buffer stage i - 1 used
+        int8_t* dst = smem + ((ph + rs) % S) * C::kStage;
+        if (rs < KST)
+          ld.template issue_part_at<0, L>(n0, m0, rs, dst, wv, ln);
+        else if (more)
+          ld.template issue_part_at<0, L>(n1, m1, rs - KST, dst, wv, ln);
+        else
+          ld.template issue_part_at<0, L>(n0, m0, KST - 1, dst, wv, ln);
+      }
+      const bool xst = stored && i <= S - 3;  // previous epilogue's stores after stage i + 1
+      if (grp == 1) {
+        if (xst) wait_vm<(S - 2) * L + kStores>(); else wait_vm<(S - 2) * L>();
+      }
+      block_barrier();
+      // ---- compute phase of step i
+      sched_fence();
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int fi = 0; fi < C::FN; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < C::FM; ++fj) acc[fi][fj] = C::Op::run(f.w[fi], f.x[fj], acc[fi][fj]);
+      __builtin_amdgcn_s_setprio(0);
+      sched_fence();
+      if (grp == 0) {
+        if (xst) wait_vm<(S - 2) * L + kStores>(); else wait_vm<(S - 2) * L>();
+      }
+      block_barrier();
+    }
+    ph = (ph + KST) % S;
+    // after the last tile the repeated stages must land before the
+    // workgroup's LDS is released
+    if (!more) wait_vm0();
+    int ln2 = lane, wv2 = wave;
+    asm volatile("" : "+v"(ln2), "+s"(wv2));
+    if constexpr (OUT_I32)
+      epilogue<C, true, false>(a, m0, n0, wv2 % C::WN, wv2 / C::WN, ln2, acc);
+    else
+      epilogue_fast<C, EPI>(a, m0, n0, wv2 % C::WN, wv2 / C::WN, ln2, acc, epi);
+    stored = true;
+    par ^= 1;
+    if (!more) break;
+    t = tnext;
+    m0 = m1;
+    n0 = n1;
+  }
+  // group 1 passed one barrier more than group 0
+  if (grp == 0) block_barrier();
+}
+
 // ----------------------------------------------------------- few tokens --
 // A GEMM with a handful of token rows is bound by streaming the weights from
 // HBM once (M = 1 .. 16: 2 .. 32 ops per weight byte).  Each workgroup owns
@@ -1386,6 +1551,10 @@ using C6 = Tile<16, 64, 1, 4, 128, 2, 16>;    // wave tile 16 x 16 (skinny M)
 using C7 = Tile<256, 192, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 96(n)
 using C9 = Tile<256, 256, 2, 2, 64, 4, 16>;   // C0 on 16x16x64 blocks, one k-step per stage
 using C10 = Tile<256, 192, 2, 2, 64, 4, 16>;  // C7 on 16x16x64 blocks
+using C11 = Tile<256, 256, 2, 4, 64, 4, 16>;  // C9 with 8 waves (2 per SIMD), wave tile 128 x 64
+// configuration 12: C11's tile on the ping-pong kernel (gemm_pp_kernel) for
+// interior tiles; its edge tiles, and shapes with K < STAGES x BK, take C11's
+// own kernels
 
 const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 0.97f},
@@ -1399,6 +1568,8 @@ const ConfigInfo kConfigs[] = {
     {"few_rows_splitk4_mf16", 16, 16, 256, 8, 0.10f},
     {"bm256_bn256_bk64_s4_mf16", 256, 256, 256, 1, 1.00f},
     {"bm256_bn192_bk64_s4_mf16", 256, 192, 256, 1, 0.93f},
+    {"bm256_bn256_bk64_s4_mf16_w8", 256, 256, 512, 1, 0.99f},
+    {"bm256_bn256_bk64_s4_mf16_pp", 256, 256, 512, 1, 1.05f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kSkinny = 6;    // 16-row tiled kernel
@@ -1470,6 +1641,42 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
     gemm_kernel<C, I32, true><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
         a, static_cast<int>(E), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),
         static_cast<int>(NTi), interior ? 0 : 1);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+// Ping-pong launch: interior tiles (whole stages in K, at least STAGES of
+// them, aligned vectors) on gemm_pp_kernel, the ragged edge on the tile
+// configuration's own edge kernel; shapes that do not meet the interior
+// conditions run wholly on the configuration's own kernels.
+template <class C, bool I32>
+hipError_t launch_pp(const GemmArgs& a, hipStream_t stream) {
+  const int64_t MT = (a.M + C::BM - 1) / C::BM;
+  const int64_t NT = (a.N + C::BN - 1) / C::BN;
+  if (MT * NT > INT32_MAX) return hipErrorInvalidValue;
+  const bool epi = C::kEpiLds && !I32;
+  const bool interior = (a.N % 8 == 0) && (a.K % C::BK == 0) && (a.K / C::BK >= C::STAGES) &&
+                        (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
+                        (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0) &&
+                        (!epi || (reinterpret_cast<uintptr_t>(a.sx) % 16 == 0 &&
+                                  reinterpret_cast<uintptr_t>(a.bias) % 16 == 0));
+  const int64_t MTi = a.M / C::BM, NTi = a.N / C::BN, Ti = MTi * NTi;
+  if (!interior || Ti == 0) return launch_cfg<C, I32>(a, stream);
+  int grid = 0;
+  hipError_t e = persistent_grid<gemm_pp_kernel<C, I32>>(C::kThreads, Ti, grid);
+  if (e != hipSuccess) return e;
+  gemm_pp_kernel<C, I32><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
+      a, static_cast<int>(Ti), static_cast<int>(MTi), static_cast<int>(NTi));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t E = (MT > MTi ? NT : 0) + (NT > NTi ? MTi : 0);
+  if (E > 0) {
+    e = persistent_grid<gemm_kernel<C, I32, true>>(C::kThreads, E, grid);
+    if (e != hipSuccess) return e;
+    gemm_kernel<C, I32, true><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
+        a, static_cast<int>(E), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),
+        static_cast<int>(NTi), 0);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -1602,6 +1809,8 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 8: return launch_few_rows_any(a, out_int32, stream);
     case 9: return launch_cfg_out<C9>(a, out_int32, stream);
     case 10: return launch_cfg_out<C10>(a, out_int32, stream);
+    case 11: return launch_cfg_out<C11>(a, out_int32, stream);
+    case 12: return out_int32 ? launch_pp<C11, true>(a, stream) : launch_pp<C11, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
