@@ -61,7 +61,8 @@ enum w8a8_status {
   W8A8_ERR_K_OVERFLOW = 4, /* K > W8A8_MAX_K: int32 accumulation could overflow */
   W8A8_ERR_WORKSPACE = 5,  /* workspace NULL or smaller than required */
   W8A8_ERR_HIP = 6,        /* the HIP runtime rejected a launch */
-  W8A8_ERR_CONFIG = 7      /* unknown GEMM kernel configuration id */
+  W8A8_ERR_CONFIG = 7,     /* unknown GEMM kernel configuration id */
+  W8A8_ERR_SCRATCH = 8     /* w8a8_linear_noalloc: problem exceeds its static scratch */
 };
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -136,6 +137,26 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
 int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w,
                 const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The fused linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and result as w8a8_linear, with the activation codes
+ * and scales kept in a static device scratch array of the library instead of
+ * a caller workspace.  Nothing is allocated by the call (no hipMalloc or
+ * allocating library routine); each GPU holds its own copy of the array,
+ * w8a8_linear_noalloc_max_bytes() = 64 MiB, from its first use until the
+ * process ends.  Problems whose codes and scales exceed it
+ * (w8a8_linear_workspace_bytes(M, K) > w8a8_linear_noalloc_max_bytes()) fail
+ * with W8A8_ERR_SCRATCH.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams, or threads without
+ * ordering) race on it and must be ordered by the caller.  On return the
+ * array holds this call's codes and scales; nothing in it needs clearing.
+ */
+int w8a8_linear_noalloc(const void* x_bf16, const int8_t* w_q, const float* s_w,
+                        const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
+                        void* stream);
+size_t w8a8_linear_noalloc_max_bytes(void);
 
 /*
  * GELU followed by per-token quantization, for the activation between the

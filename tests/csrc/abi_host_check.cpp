@@ -46,6 +46,11 @@ hipError_t launch_gemm(const GemmArgs& a, bool i32, int cfg, hipStream_t) {
   ++g_gemm;
   return hipSuccess;
 }
+alignas(256) unsigned char g_scratch_stub[1024];
+hipError_t noalloc_scratch(void** ptr) {
+  *ptr = g_scratch_stub;  // stands in for the device scratch
+  return hipSuccess;
+}
 int gemm_fp8_num_configs() { return 6; }
 const char* gemm_fp8_config_name(int c) { return (c >= 0 && c < 6) ? "stub" : nullptr; }
 int gemm_fp8_select_config(int64_t, int64_t, int64_t) { return 4; }
@@ -68,7 +73,7 @@ int main() {
   std::vector<uint16_t> y(M * N);
   alignas(16) static unsigned char ws_buf[8192];
 
-  for (int s = 0; s < 8; ++s) CHECK(w8a8_status_string(s) != nullptr);
+  for (int s = 0; s < 9; ++s) CHECK(w8a8_status_string(s) != nullptr);
   CHECK(w8a8_status_string(-1) != nullptr && w8a8_status_string(99) != nullptr);
 
   // quantize_act
@@ -140,6 +145,19 @@ int main() {
                     sizeof(ws_buf), nullptr) == W8A8_ERR_WORKSPACE);
   CHECK(g_quant == 4 && g_gemm == 4);
 
+  // allocation-free fused linear: the static scratch instead of a workspace
+  CHECK(w8a8_linear_noalloc_max_bytes() == (size_t{64} << 20));
+  CHECK(w8a8_linear_noalloc(x.data(), wq.data(), sw.data(), bias.data(), M, N, K, y.data(), nullptr) ==
+        W8A8_OK);
+  CHECK(g_quant == 5 && g_gemm == 5 && g_last.qx == reinterpret_cast<int8_t*>(w8a8::g_scratch_stub));
+  CHECK(w8a8_linear_noalloc(x.data(), wq.data(), sw.data(), bias.data(), 1 << 20, N, 128, y.data(),
+                            nullptr) == W8A8_ERR_SCRATCH);
+  CHECK(w8a8_linear_noalloc(x.data(), wq.data(), sw.data(), bias.data(), M, N, 40, y.data(), nullptr) ==
+        W8A8_ERR_SHAPE);
+  CHECK(w8a8_linear_noalloc(x.data(), wq.data(), sw.data(), bias.data(), 0, N, K, y.data(), nullptr) ==
+        W8A8_OK);
+  CHECK(g_quant == 5 && g_gemm == 5);
+
   // FP8 entries
   uint8_t* q8 = reinterpret_cast<uint8_t*>(q.data());
   uint8_t* w8 = reinterpret_cast<uint8_t*>(wq.data());
@@ -155,7 +173,7 @@ int main() {
         W8A8_OK);
   CHECK(w8a8_linear_fp8(x.data(), w8, sw.data(), nullptr, M, N, K, y.data(), ws_buf, 16, nullptr) ==
         W8A8_ERR_WORKSPACE);
-  CHECK(g_gemm_fp8 == 2 && g_quant == 8);
+  CHECK(g_gemm_fp8 == 2 && g_quant == 9);
 
   // configuration tables
   CHECK(w8a8_gemm_num_configs() == 11 && w8a8_gemm_fp8_num_configs() == 6);

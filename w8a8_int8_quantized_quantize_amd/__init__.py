@@ -49,6 +49,8 @@ def _load() -> ctypes.CDLL:
         "w8a8_gemm_dequant": ([P, P, P, P, P, I64, I64, I64, P, P], I),
         "w8a8_linear_workspace_bytes": ([I64, I64], ctypes.c_size_t),
         "w8a8_linear": ([P, P, P, P, I64, I64, I64, P, P, ctypes.c_size_t, P], I),
+        "w8a8_linear_noalloc": ([P, P, P, P, I64, I64, I64, P, P], I),
+        "w8a8_linear_noalloc_max_bytes": ([], ctypes.c_size_t),
         "w8a8_gelu_quantize_act": ([P, I64, I64, I64, P, I64, P, P, P], I),
         "w8a8_gemm_num_configs": ([], I),
         "w8a8_gemm_config_name": ([I], ctypes.c_char_p),
@@ -267,6 +269,36 @@ def w8a8_linear(x, w_q, s_w, bias=None, out=None, workspace=None):
     rc = _lib.w8a8_linear(_ptr(x), _ptr(w_q), _ptr(s_w), _ptr(bias), M, N, K, _ptr(out),
                           _ptr(workspace), workspace.numel(), _stream(x.device))
     _check(rc, "w8a8_linear")
+    return out
+
+
+def w8a8_linear_noalloc_max_bytes() -> int:
+    return int(_lib.w8a8_linear_noalloc_max_bytes())
+
+
+def w8a8_linear_noalloc(x, w_q, s_w, bias=None, out=None):
+    """The fused W8A8 linear without a workspace: the activation codes and
+    scales go to the library's static device scratch (for callers that cannot
+    allocate; calls on one GPU must be ordered).  bf16 x [M, K] -> bf16 y."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w_q, "w_q", torch.int8, 2)
+    M, K = x.shape
+    N, K2 = w_q.shape
+    if K != K2:
+        raise ValueError(f"K mismatch: x {tuple(x.shape)} vs w_q {tuple(w_q.shape)}")
+    if not (x.is_contiguous() and w_q.is_contiguous()):
+        raise ValueError("x and w_q must be contiguous")
+    _vec(s_w, "s_w", torch.float32, N)
+    _vec(bias, "bias", torch.bfloat16, N)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [M, N] bf16 tensor")
+    _same_device(x, w_q, s_w, bias, out)
+    with torch.cuda.device(x.device):
+        rc = _lib.w8a8_linear_noalloc(_ptr(x), _ptr(w_q), _ptr(s_w), _ptr(bias), M, N, K, _ptr(out),
+                                      _stream(x.device))
+    _check(rc, "w8a8_linear_noalloc")
     return out
 
 

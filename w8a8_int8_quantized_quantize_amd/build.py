@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libw8a8.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "noalloc.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

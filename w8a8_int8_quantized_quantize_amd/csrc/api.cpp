@@ -128,6 +128,9 @@ const char* w8a8_status_string(int status) {
     case W8A8_ERR_WORKSPACE: return "W8A8_ERR_WORKSPACE: workspace NULL or too small";
     case W8A8_ERR_HIP: return "W8A8_ERR_HIP: the HIP runtime rejected a launch";
     case W8A8_ERR_CONFIG: return "W8A8_ERR_CONFIG: unknown GEMM configuration";
+    case W8A8_ERR_SCRATCH:
+      return "W8A8_ERR_SCRATCH: codes and scales of x exceed the no-alloc entry's static scratch "
+             "(w8a8_linear_noalloc_max_bytes)";
     default: return "W8A8: unknown status";
   }
 }
@@ -205,6 +208,21 @@ int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w, const v
     return rc;
   return gemm_any(qx, sx, w_q, s_w, bias_bf16, M, N, K, y_bf16, false, -1, stream);
 }
+
+int w8a8_linear_noalloc(const void* x_bf16, const int8_t* w_q, const float* s_w,
+                        const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,
+                        void* stream) {
+  if (M < 0 || N < 0) return W8A8_ERR_SHAPE;
+  if (int rc = check_k(K)) return rc;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (w8a8_linear_workspace_bytes(M, K) > w8a8::kNoAllocScratchBytes) return W8A8_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (w8a8::noalloc_scratch(&scratch) != hipSuccess) return W8A8_ERR_HIP;
+  return w8a8_linear(x_bf16, w_q, s_w, bias_bf16, M, N, K, y_bf16, scratch,
+                     w8a8::kNoAllocScratchBytes, stream);
+}
+
+size_t w8a8_linear_noalloc_max_bytes(void) { return w8a8::kNoAllocScratchBytes; }
 
 int w8a8_quantize_act_fp8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                           int64_t ldq, float* scale, void* stream) {

@@ -43,4 +43,11 @@ const char* gemm_fp8_config_name(int cfg);
 int gemm_fp8_select_config(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_fp8(const GemmArgs& a, int cfg, hipStream_t stream);
 
+// ------------------------------------------------------ no-alloc scratch --
+// Bytes of the static device scratch behind w8a8_linear_noalloc (codes and
+// scales of the activations, laid out as w8a8_linear's workspace).
+constexpr size_t kNoAllocScratchBytes = size_t{64} << 20;
+// This device's address of that scratch (looked up once per device).
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace w8a8
