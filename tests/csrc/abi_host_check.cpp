@@ -51,6 +51,13 @@ hipError_t noalloc_scratch(void** ptr) {
   *ptr = g_scratch_stub;  // stands in for the device scratch
   return hipSuccess;
 }
+int g_rows = 0;
+bool linear_few_rows_supported(int64_t M, int64_t, int64_t K) { return M <= 2 && K <= 3072; }
+hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t) {
+  CHECK(a.M >= 1 && a.M <= 2 && a.qx_out != nullptr && a.sx_out != nullptr && a.y != nullptr);
+  ++g_rows;
+  return hipSuccess;
+}
 int gemm_fp8_num_configs() { return 6; }
 const char* gemm_fp8_config_name(int c) { return (c >= 0 && c < 6) ? "stub" : nullptr; }
 int gemm_fp8_select_config(int64_t, int64_t, int64_t) { return 4; }
@@ -144,6 +151,11 @@ int main() {
   CHECK(w8a8_linear(x.data(), wq.data(), sw.data(), bias.data(), INT64_MAX, N, K, y.data(), ws_buf,
                     sizeof(ws_buf), nullptr) == W8A8_ERR_WORKSPACE);
   CHECK(g_quant == 4 && g_gemm == 4);
+
+  // a handful of tokens: the single-launch fused kernel, codes into the workspace
+  CHECK(w8a8_linear(x.data(), wq.data(), sw.data(), bias.data(), 2, N, K, y.data(), ws_buf, need,
+                    nullptr) == W8A8_OK);
+  CHECK(w8a8::g_rows == 1 && g_quant == 4 && g_gemm == 4);
 
   // allocation-free fused linear: the static scratch instead of a workspace
   CHECK(w8a8_linear_noalloc_max_bytes() == (size_t{64} << 20));

@@ -382,3 +382,33 @@ def test_full_size_dit_block_chain():
     c3 = oracle.linear_prequant(qo2, so2, wqo, swo, b)["y"]
     from gpu_helpers import cosine
     assert cosine(y3, c3) >= 0.99999
+
+
+# A handful of token rows: w8a8_linear runs quantization, GEMM and epilogue in
+# one launch (M <= 4, K <= 3072; two launches for more rows) and leaves the
+# codes and scales in its workspace either way.  Rows include an all-zero row and one whose scale
+# is subnormal (the division path of the quantizer), K with a ragged 64-element
+# step, and N not a multiple of 16.
+@pytest.mark.parametrize("M,N,K", [(1, 3072, 3072), (4, 3072, 3072), (3, 100, 1040), (3, 16, 16),
+                                   (1, 18432, 3072), (2, 40, 48), (4, 272, 2000), (1, 16, 3072),
+                                   (16, 3072, 3072), (9, 272, 2000)])
+def test_few_rows_single_launch_linear_and_workspace(M, N, K):
+    rng = np.random.default_rng(M * 100 + K + N)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    if M >= 3:
+        xb[1] = 0                                    # all-zero row
+        xb[2] = rand_bits(rng, 1, K, scale=1e-39)[0]  # subnormal-range row
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0]
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    wqo, swo = oracle.quantize_rows_f32(w)
+    ws = torch.full((w8.w8a8_linear_workspace_bytes(M, K),), 0x55, dtype=torch.uint8, device=DEV)
+    for bias in (dev_bf16(bb), None):
+        y = w8.w8a8_linear(dev_bf16(xb), wq, sw, bias, workspace=ws)
+        want = oracle.linear(xb, wqo, swo, bb if bias is not None else None)
+        assert np.array_equal(bits(y), want["y"])
+        pad = (M * K + 255) // 256 * 256
+        codes = host(ws[:M * K]).view(np.int8).reshape(M, K)
+        scales = host(ws[pad:pad + 4 * M]).view(np.float32)
+        assert np.array_equal(codes, want["q_x"])
+        assert np.array_equal(scales.view(np.uint32), want["s_x"].view(np.uint32))

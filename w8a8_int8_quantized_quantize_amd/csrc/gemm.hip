@@ -53,6 +53,7 @@
 // and zeroed in the activation fragment before the MFMA.  K is a multiple of
 // 16 (API contract), so a chunk is entirely inside or outside K.
 #include "internal.h"
+#include "quant_codes.h"
 
 #include <algorithm>
 #include <atomic>
@@ -1502,6 +1503,176 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
   }
 }
 
+// ------------------------------------------- few tokens, fused quantize --
+// The whole fused linear for M <= 16 token rows in one launch.  Each
+// workgroup owns 16 output columns; its 4 waves split K for the MFMAs as in
+// gemm_few_rows.  Before them, the workgroup quantizes the M x K activations
+// itself: its 256 threads take the 16-byte chunks of x [M, K] in turn, reduce
+// each row's absmax in LDS (an atomic max on the magnitude's bit pattern,
+// exact in any order), and write the codes, computed with the row
+// quantizer's own operations (quant_codes.h, the same bits
+// w8a8_quantize_act writes), into an LDS copy of the codes; each lane then
+// reads its MFMA operand from there.  The activations are loaded before the
+// weight fragments (loads complete in issue order), so they are quantized
+// while the weights stream in.  Every workgroup reads all of x (at most
+// 16 x 3072 bf16, L2-resident after the first), in place of a separate
+// quantize launch and the gap before the GEMM's.  Column block 0 also writes
+// the codes and scales to the workspace, as the two-launch path does.
+//   MFMA 16x16x64 layout: lane l holds token row l % 16 and K bytes
+//   16 (l / 16) .. +15 of a 64-byte step: one 16-byte LDS read.
+// LDS copy of the codes: row stride K + 16 bytes, so that the 16 rows of a
+// fragment read fall in 16 different 16-byte bank groups.
+constexpr int kRowsMaxK = 3072;  // codes of 16 rows of up to this K fit the LDS copy
+// Every workgroup quantizes all M rows, so the redundant work grows with M:
+// the single launch is taken for up to 4 rows (measured slower than the two
+// launches at 16 rows, where each workgroup quantizes 49152 elements).
+constexpr int kRowsMaxM = 4;
+template <int CH, int ST>
+__global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) int8_t codes[16 * (kRowsMaxK + 16)];
+  __shared__ v4i part[NW][64];
+  __shared__ uint32_t amax_bits[16];
+  __shared__ float srow[16];
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int t = threadIdx.x;
+  const int64_t M = a.M, N = a.N, K = a.K;
+  const int64_t ldc = K + 16;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int r = lane % 16, kq = lane / 16;
+  const int64_t steps = (K + 63) / 64;
+  const int64_t per = (steps + NW - 1) / NW;
+  const int64_t s0 = wave * per, s1 = min(steps, s0 + per);
+  if (t < 16) amax_bits[t] = 0u;
+  // epilogue scales and bias (clamped columns past N)
+  float swe[4];
+  uint32_t braw[4];
+  {
+    const uint16_t* bsrc = a.bias ? a.bias : reinterpret_cast<const uint16_t*>(a.sw);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t n = min(n0 + 4 * kq + e, N - 1);
+      swe[e] = a.sw[n];
+      braw[e] = bsrc[n];
+    }
+  }
+  // this thread's chunks of x: flat chunk index c = t + 256 j over [M, K / 8];
+  // its row and position follow incrementally (no division per chunk)
+  const int ck = static_cast<int>(K / 8);  // chunks per row (K <= kRowsMaxK)
+  const int total = static_cast<int>(M) * ck;
+  const int q256 = 256 / ck, r256 = 256 % ck;
+  const int row0 = t / ck, pos0 = t % ck;
+  uint4 xv[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = t + 256 * j;
+    const int cc = c < total ? c : total - 1;  // clamped: a copy of a real chunk
+    xv[j] = reinterpret_cast<const uint4*>(a.x)[cc];
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the weight fragments of this wave's K share (past the share or past K:
+  // clamped to offset 0, never used)
+  const int8_t* wrow = a.qw + min(n0 + r, N - 1) * K;
+  v4i wf[ST];
+#pragma unroll
+  for (int i = 0; i < ST; ++i) {
+    const int64_t k = (s0 + i) * 64 + kq * 16;
+    const int64_t kc = ((s0 + i) < s1 && k < K) ? k : 0;
+    wf[i] = *reinterpret_cast<const v4i*>(wrow + kc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();  // amax_bits cleared
+  // row absmax: the magnitude bits of the largest element (non-negative
+  // values order as their bit patterns).  Chunk t + 256 j lies in row
+  // (row, pos), followed incrementally from (row0, pos0).
+  {
+    int row = row0, pos = pos0;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      if (t + 256 * j < total) {
+        u16x2 m2 = {0, 0};
+        m2 = absmax2(absmax2(absmax2(absmax2(m2, xv[j].x), xv[j].y), xv[j].z), xv[j].w);
+        atomicMax(&amax_bits[row], __float_as_uint(absmax_of(m2)));
+      }
+      row += q256;
+      pos += r256;
+      if (pos >= ck) {
+        pos -= ck;
+        ++row;
+      }
+    }
+  }
+  __syncthreads();
+  if (t < 16 && t < M) srow[t] = __uint_as_float(amax_bits[t]) / 127.0f;
+  __syncthreads();
+  // codes into the LDS copy
+  int row = row0, pos = pos0;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    if (t + 256 * j < total) {
+      const float s = srow[row];
+      uint2 p = make_uint2(0u, 0u);
+      if (s >= kFastMinScale) {
+        const float rcp = 1.0f / s;
+        p.x = pack4(code_word<2>(bf_lo(xv[j].x), s, rcp), code_word<2>(bf_hi(xv[j].x), s, rcp),
+                    code_word<2>(bf_lo(xv[j].y), s, rcp), code_word<2>(bf_hi(xv[j].y), s, rcp));
+        p.y = pack4(code_word<2>(bf_lo(xv[j].z), s, rcp), code_word<2>(bf_hi(xv[j].z), s, rcp),
+                    code_word<2>(bf_lo(xv[j].w), s, rcp), code_word<2>(bf_hi(xv[j].w), s, rcp));
+      } else if (s != 0.0f) {
+        p.x = pack4(code_word<1>(bf_lo(xv[j].x), s, 0.f), code_word<1>(bf_hi(xv[j].x), s, 0.f),
+                    code_word<1>(bf_lo(xv[j].y), s, 0.f), code_word<1>(bf_hi(xv[j].y), s, 0.f));
+        p.y = pack4(code_word<1>(bf_lo(xv[j].z), s, 0.f), code_word<1>(bf_hi(xv[j].z), s, 0.f),
+                    code_word<1>(bf_lo(xv[j].w), s, 0.f), code_word<1>(bf_hi(xv[j].w), s, 0.f));
+      }
+      *reinterpret_cast<uint2*>(codes + row * ldc + pos * 8) = p;
+      if (blockIdx.x == 0 && a.qx_out != nullptr)
+        *reinterpret_cast<uint2*>(a.qx_out + row * K + pos * 8) = p;
+    }
+    row += q256;
+    pos += r256;
+    if (pos >= ck) {
+      pos -= ck;
+      ++row;
+    }
+  }
+  if (blockIdx.x == 0 && a.sx_out != nullptr && t < M) a.sx_out[t] = srow[t];
+  __syncthreads();
+  // MFMAs over the wave's K share; rows past M read row M - 1 of the copy
+  const int8_t* crow_l = codes + min<int64_t>(r, M - 1) * ldc;
+  v4i acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < ST; ++i) {
+    if (s0 + i >= s1) break;  // wave-uniform
+    const int64_t k = (s0 + i) * 64 + kq * 16;
+    v4i xq = {0, 0, 0, 0};
+    if (k < K) xq = *reinterpret_cast<const v4i*>(crow_l + k);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], xq, acc, 0, 0, 0);
+  }
+  part[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || r >= M) return;
+  v4i tt = part[0][lane];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) tt += part[w][lane];
+  const float s = srow[r];
+  const int64_t nb = n0 + 4 * kq;
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float bv = a.bias ? __uint_as_float(braw[e] << 16) : -0.0f;
+    v[e] = dequant(tt[e], s, swe[e], bv);
+  }
+  uint16_t* out = a.y + r * N + nb;
+  if (N % 4 == 0 && nb + 3 < N) {
+    *reinterpret_cast<uint2*>(out) = make_uint2(bf16_pair(v[0], v[1]), bf16_pair(v[2], v[3]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (nb + e < N) out[e] = static_cast<uint16_t>(bf16_bits(v[e]));
+  }
+}
+
 template <int NW, int NB, bool I32, int ST, bool LOOP = false, bool FP8 = false>
 hipError_t launch_few_rows_st(const GemmArgs& a, hipStream_t stream) {
   const int64_t gx = (a.N + 16 * NB - 1) / (16 * NB), gy = (a.M + 15) / 16;
@@ -1526,6 +1697,25 @@ hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
   if (per <= 8) return launch_few_rows_st<NW, NB, I32, 8, false, FP8>(a, stream);
   if (per <= 12) return launch_few_rows_st<NW, NB, I32, 12, false, FP8>(a, stream);
   return launch_few_rows_st<NW, NB, I32, 12, true, FP8>(a, stream);
+}
+
+template <int CH, int ST>
+hipError_t launch_linear_few_rows_st(const RowsArgs& a, hipStream_t stream) {
+  const int64_t gx = (a.N + 15) / 16;
+  if (gx > INT32_MAX) return hipErrorInvalidValue;
+  linear_few_rows<CH, ST><<<dim3(static_cast<unsigned>(gx)), dim3(256), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// Chunks of x per thread: CH covering M x K / 8 over 256 threads.
+template <int ST>
+hipError_t launch_linear_few_rows_ch(const RowsArgs& a, hipStream_t stream) {
+  const int64_t ch = (a.M * (a.K / 8) + 255) / 256;
+  if (ch <= 1) return launch_linear_few_rows_st<1, ST>(a, stream);
+  if (ch <= 2) return launch_linear_few_rows_st<2, ST>(a, stream);
+  if (ch <= 4) return launch_linear_few_rows_st<4, ST>(a, stream);
+  if (ch <= 6) return launch_linear_few_rows_st<6, ST>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_few_rows_any(const GemmArgs& a, bool i32, hipStream_t stream) {
@@ -1840,6 +2030,27 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 3: return launch_few_rows<4, 1, false, true>(a, stream);
     case 4: return launch_cfg<F3, false>(a, stream);
     case 5: return launch_cfg<F4, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The single-launch fused linear takes M <= 16 rows whose K fits one chunk
+// of at most 12 64-element steps per wave (K <= 3072 with 4 waves), where the
+// library would run the few-row GEMM.
+bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > kRowsMaxM || N < 1 || K < 16 || K % 16 != 0 || K > kRowsMaxK) return false;
+  return gemm_select_config(M, N, K) == kFewRows;
+}
+
+hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t stream) {
+  const int64_t per = ((a.K + 63) / 64 + 3) / 4;  // 64-byte steps per wave
+  switch (per) {
+    case 1: return launch_linear_few_rows_ch<1>(a, stream);
+    case 2: return launch_linear_few_rows_ch<2>(a, stream);
+    case 3: case 4: return launch_linear_few_rows_ch<4>(a, stream);
+    case 5: case 6: return launch_linear_few_rows_ch<6>(a, stream);
+    case 7: case 8: return launch_linear_few_rows_ch<8>(a, stream);
+    case 9: case 10: case 11: case 12: return launch_linear_few_rows_ch<12>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

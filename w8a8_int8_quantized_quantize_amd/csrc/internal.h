@@ -30,6 +30,21 @@ struct GemmArgs {
   int64_t M, N, K;
 };
 
+// The fused linear for a handful of token rows in one launch (quantize +
+// GEMM + epilogue); the codes and scales of x also go to qx_out / sx_out.
+struct RowsArgs {
+  const uint16_t* x;     // [M, K] bf16 activations, row stride K
+  const int8_t* qw;      // [N, K] weight codes
+  const float* sw;       // [N]
+  const uint16_t* bias;  // [N] bf16 or nullptr
+  uint16_t* y;           // [M, N] bf16
+  int8_t* qx_out;        // [M, K] codes of x, or nullptr
+  float* sx_out;         // [M] scales of x, or nullptr
+  int64_t M, N, K;
+};
+bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t stream);
+
 int gemm_num_configs();
 const char* gemm_config_name(int cfg);
 int gemm_select_config(int64_t M, int64_t N, int64_t K);

@@ -1,0 +1,63 @@
+// Device helpers of the row quantization shared by the quantize kernels and
+// the fused few-row linear: both compute a token's codes with exactly these
+// operations, so the codes of one row are the same bits whichever kernel
+// computes them.  Convention (open on the pages, fixed here): scale =
+// fl32(absmax / 127); code = clamp(rne(fl32(x / scale)), -127, 127); a row
+// whose scale is 0 gets all-zero codes.  ("Realizing Native INT8 Compute for
+// Diffusion Transformers on Consumer GPUs", Abstract: per-token activation
+// quantization.)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+// Scales from here up take the reciprocal quotient with one Markstein
+// correction, which equals the IEEE division's code for every pair of bf16
+// values |x| <= absmax (checked exhaustively on the CPU); smaller scales
+// take the IEEE division.
+constexpr float kFastMinScale = 0x1p-96f;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Packed |x| max of two bf16 values per 32-bit word.
+__device__ __forceinline__ u16x2 absmax2(u16x2 m, uint32_t w) {
+  const uint32_t a = w & 0x7FFF7FFFu;
+  return __builtin_elementwise_max(m, *reinterpret_cast<const u16x2*>(&a));
+}
+
+__device__ __forceinline__ float absmax_of(u16x2 m) {
+  const uint32_t b = m.x > m.y ? m.x : m.y;
+  return __uint_as_float(b << 16);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Code of x as the low byte of the returned word.  MODE 0: s == 0 (all
+// zero); MODE 1: IEEE division, clamped to [-127, 127] (a subnormal scale can
+// be far below absmax / 127); MODE 2: reciprocal + Markstein correction, no
+// clamp: there s >= 2^-96 is within 2^-24 of absmax / 127, so |x / s| for
+// |x| <= absmax stays below 127.5 and rounds into [-127, 127] by itself.
+template <int MODE>
+__device__ __forceinline__ uint32_t code_word(float x, float s, float r) {
+  float t;
+  if constexpr (MODE == 0) {
+    return 0u;
+  } else if constexpr (MODE == 1) {
+    t = __builtin_amdgcn_fmed3f(x / s, -127.0f, 127.0f);
+  } else {
+    const float q = x * r;
+    t = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+  }
+  return __float_as_uint(t + 12582912.0f);
+}
+
+__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+}  // namespace w8a8

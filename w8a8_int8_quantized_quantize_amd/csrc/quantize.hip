@@ -41,6 +41,7 @@
 // Exactness: built with correctly rounded fp32 division, fp32 denormals kept
 // and contraction off, so every step matches the IEEE definition bit for bit.
 #include "internal.h"
+#include "quant_codes.h"
 
 namespace w8a8 {
 namespace {
@@ -51,13 +52,11 @@ constexpr int64_t kMaxBlocks = 1 << 20;   // grid cap; rows are grid-strided
 constexpr int kLutWaves = 16;             // GELU kernels: one workgroup per CU
 constexpr int kLutThreads = 64 * kLutWaves;
 constexpr int kLutMaxBlocks = 256;        // persistent: one per compute unit
-constexpr float kFastMinScale = 0x1p-96f;
 
 __device__ const uint16_t kGeluLut[65536] __attribute__((aligned(16))) = {
 #include "gelu_lut.inc"
 };
 
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Wave index within the workgroup, in a scalar register (so row bases are
@@ -70,17 +69,6 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
-}
-
-// Packed |x| max of two bf16 values per 32-bit word.
-__device__ __forceinline__ u16x2 absmax2(u16x2 m, uint32_t w) {
-  const uint32_t a = w & 0x7FFF7FFFu;
-  return __builtin_elementwise_max(m, *reinterpret_cast<const u16x2*>(&a));
-}
-
-__device__ __forceinline__ float absmax_of(u16x2 m) {
-  const uint32_t b = m.x > m.y ? m.x : m.y;
-  return __uint_as_float(b << 16);
 }
 
 // Element c of a row through a 32-bit byte offset from the row's (scalar)
@@ -108,34 +96,6 @@ __device__ __forceinline__ void load_row(const uint4* src, uint32_t nch, uint32_
     raw[j] = at(src, c < nch ? c : nch - 1);
     __builtin_amdgcn_sched_barrier(0);  // issue order = chunk order
   }
-}
-
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// Code of x as the low byte of the returned word.  MODE 0: s == 0 (all
-// zero); MODE 1: IEEE division, clamped to [-127, 127] (a subnormal scale can
-// be far below absmax / 127); MODE 2: reciprocal + Markstein correction, no
-// clamp: there s >= 2^-96 is within 2^-24 of absmax / 127, so |x / s| for
-// |x| <= absmax stays below 127.5 and rounds into [-127, 127] by itself.
-template <int MODE>
-__device__ __forceinline__ uint32_t code_word(float x, float s, float r) {
-  float t;
-  if constexpr (MODE == 0) {
-    return 0u;
-  } else if constexpr (MODE == 1) {
-    t = __builtin_amdgcn_fmed3f(x / s, -127.0f, 127.0f);
-  } else {
-    const float q = x * r;
-    t = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
-  }
-  return __float_as_uint(t + 12582912.0f);
-}
-
-__device__ __forceinline__ uint32_t pack4(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
-  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
-  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // FP8 (OCP e4m3) codes of four quotients: each clamped to the largest finite
