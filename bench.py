@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--compare", action="store_true",
                     help="per workload shape: fused INT8 linear vs the 'fake INT8' path "
                          "(quantize, dequantize to bf16, bf16 GEMM) vs a plain bf16 GEMM")
+    ap.add_argument("--profile-shapes", default="",
+                    help="comma-separated workload shape names: run the fused linear (w8a8_linear) "
+                         "on each, --iters times, weights rotated (a driver for rocprofv3 counters)")
+    ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of known size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar=("GEMM_FETCH", "GEMM_WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -339,6 +343,34 @@ def _time_calls(torch, fn, n_iter, n_copy):
     return ts[len(ts) // 2], ts[0]
 
 
+def profile_shapes(args, torch, w8, synthetic):
+    """The fused linear w8a8_linear on each named workload shape, `iters`
+    back-to-back calls with weight copies rotated past the last-level cache,
+    for rocprofv3 counter and trace runs (one dispatch per kernel per call)."""
+    dev = "cuda:0"
+    names = args.profile_shapes.split(",")
+    shapes = {s.name: s for v in synthetic.CONFIGS.values() for s in v}
+    for name in names:
+        s = shapes[name]
+        st = synthetic.streams(0, s.config_id, s.layer_id)
+        x = synthetic.activations_bf16(st, s.M, s.K, s.outlier_frac).to(dev)
+        w = torch.from_numpy(synthetic.weights_f32(st, s.N, s.K)).to(dev)
+        b = synthetic.bias_bf16(st, s.N).to(dev)
+        wq, sw = w8.w8a8_quantize_weight(w)
+        del w
+        ncopy = max(1, min(64, -(-600_000_000 // (s.N * s.K))))
+        ws_ = [(wq, sw)] + [(wq.clone(), sw.clone()) for _ in range(ncopy - 1)]
+        y = torch.empty((s.M, s.N), dtype=torch.bfloat16, device=dev)
+        work = torch.empty((w8.w8a8_linear_workspace_bytes(s.M, s.K),), dtype=torch.uint8, device=dev)
+        med, mn = _time_calls(torch, lambda i: w8.w8a8_linear(x, ws_[i][0], ws_[i][1], b, out=y, workspace=work),
+                              args.iters, ncopy)
+        cfg = w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(s.M, s.N, s.K))
+        print(json.dumps({"profile_shape": name, "M": s.M, "K": s.K, "N": s.N, "gemm_config": cfg,
+                          "linear_us_median": round(med, 2), "linear_us_min": round(mn, 2),
+                          "calls": args.iters + 3}), flush=True)
+        del ws_, x, y, work
+
+
 def fake_int8_forward(w8, x, wq, sw, bias, operands=False):
     """The "fake INT8" forward the pages start from (Abstract; news write-up,
     second paragraph): the same per-token int8 quantization of x, then the
@@ -444,6 +476,9 @@ def main():
         return 0
     if args.compare:
         compare(args, torch, w8, synthetic)
+        return 0
+    if args.profile_shapes:
+        profile_shapes(args, torch, w8, synthetic)
         return 0
 
     up, down, inp = make_inputs(torch, w8, synthetic, args.rotate, args.fp8)
