@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--compare", action="store_true",
                     help="per workload shape: fused INT8 linear vs the 'fake INT8' path "
                          "(quantize, dequantize to bf16, bf16 GEMM) vs a plain bf16 GEMM")
+    ap.add_argument("--interlayer", action="store_true",
+                    help="in-step A/B of the MLP step: GELU + quantize as its own pass vs GELU and the "
+                         "row absmax folded into the up-projection's epilogue + an absmax-given quantizer")
     ap.add_argument("--profile-shapes", default="",
                     help="comma-separated workload shape names: run the fused linear (w8a8_linear) "
                          "on each, --iters times, weights rotated (a driver for rocprofv3 counters)")
@@ -371,6 +374,54 @@ def profile_shapes(args, torch, w8, synthetic):
         del ws_, x, y, work
 
 
+def interlayer_ab(args, torch, w8, synthetic):
+    """In-step A/B of the inter-layer fusion (the MLP step with the up-proj
+    GEMM and the down-proj GEMM unchanged):
+      A: gemm_dequant(up) -> y;  gelu_quantize_act(y) -> q_h
+      B: gemm_dequant_gelu_amax(up) -> h, amax;  quantize_act_amax(h, amax) -> q_h
+    Blocks of `steps` steps alternate A, B, A, B, ... (`rounds` pairs) after
+    `warmup` steps of each; every step is bracketed by an event pair, and the
+    up-proj + inter-layer segment by another.  Reports the means per variant."""
+    up, down, inp = make_inputs(torch, w8, synthetic, args.rotate)
+    stream = torch.cuda.current_stream()
+    h = torch.empty_like(inp["y_up"])
+    amax = torch.empty((up.M,), dtype=torch.int32, device="cuda:0")
+
+    def step(i, variant, ev):
+        wu, su = inp["w_up"][i % len(inp["w_up"])]
+        wd, sd = inp["w_down"][i % len(inp["w_down"])]
+        ev[0].record(stream)
+        w8.w8a8_quantize_act(inp["x_up"], inp["q_x"], inp["s_x"])
+        if variant == "A":
+            w8.w8a8_gemm_dequant(inp["q_x"], inp["s_x"], wu, su, inp["b_up"], out=inp["y_up"])
+            w8.w8a8_gelu_quantize_act(inp["y_up"], inp["q_h"], inp["s_h"])
+        else:
+            w8.w8a8_gemm_dequant_gelu_amax(inp["q_x"], inp["s_x"], wu, su, inp["b_up"], h_out=h, amax=amax)
+            w8.w8a8_quantize_act_amax(h, amax, inp["q_h"], inp["s_h"])
+        ev[1].record(stream)
+        w8.w8a8_gemm_dequant(inp["q_h"], inp["s_h"], wd, sd, inp["b_down"], out=inp["y_down"])
+        ev[2].record(stream)
+
+    res = {"A": [[], []], "B": [[], []]}
+    for v in ("A", "B"):
+        for i in range(args.warmup):
+            step(i, v, [torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    rounds = 3
+    for r in range(rounds):
+        for v in ("A", "B"):
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                step(i, v, evs[i])
+            torch.cuda.synchronize()
+            res[v][0] += [e[0].elapsed_time(e[2]) * 1e3 for e in evs]
+            res[v][1] += [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    out = {"interlayer_ab": "dit1024_mlp", "steps_per_block": args.steps, "rounds": rounds}
+    for v, name in (("A", "gelu_quantize_pass"), ("B", "gelu_amax_epilogue")):
+        out[name] = {"step_us": round(sum(res[v][0]) / len(res[v][0]), 2),
+                     "quantize_up_gelu_quantize_us": round(sum(res[v][1]) / len(res[v][1]), 2)}
+    print(json.dumps(out), flush=True)
+
+
 def fake_int8_forward(w8, x, wq, sw, bias, operands=False):
     """The "fake INT8" forward the pages start from (Abstract; news write-up,
     second paragraph): the same per-token int8 quantization of x, then the
@@ -479,6 +530,9 @@ def main():
         return 0
     if args.profile_shapes:
         profile_shapes(args, torch, w8, synthetic)
+        return 0
+    if args.interlayer:
+        interlayer_ab(args, torch, w8, synthetic)
         return 0
 
     up, down, inp = make_inputs(torch, w8, synthetic, args.rotate, args.fp8)

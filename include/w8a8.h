@@ -176,6 +176,34 @@ int w8a8_gelu_quantize_act(const void* y_bf16, int64_t M, int64_t K, int64_t ldy
                            void* stream);
 
 /*
+ * Inter-layer fusion variant for the DiT MLP (GELU is not on the pages; the
+ * fusion follows the Abstract's principle of folding the work around the
+ * matmul into its epilogue).  w8a8_gemm_dequant_gelu_amax is
+ * w8a8_gemm_dequant whose epilogue also applies GELU, writing
+ *   h[m,n] = bf16_rne(gelu(y[m,n]))   (y the bf16 output of w8a8_gemm_dequant,
+ *                                      the same table as w8a8_gelu_quantize_act)
+ * and the row maxima amax[m] = max_n |h[m,n]| as fp32 bit patterns (uint32
+ * [M]; the call overwrites them).  w8a8_quantize_act_amax then quantizes h
+ * per token from those maxima without reducing the rows again: its codes and
+ * scales equal w8a8_quantize_act(h) bit for bit.  Together they replace
+ * w8a8_gemm_dequant + w8a8_gelu_quantize_act between the MLP's linears.
+ *   Shapes: M and N multiples of 256, K a multiple of 64 and >= 256
+ *   (W8A8_ERR_SHAPE otherwise); s_x, s_w and bias 16-byte aligned
+ *   (W8A8_ERR_ALIGN otherwise).  w8a8_quantize_act_amax: K <= 12288.
+ * Both variants move the same HBM bytes (a bf16 [M, N] tensor written and
+ * read back, then the codes); on the 4096 x 3072 -> 12288 up-projection the
+ * table gathers in the epilogue make this pair slower than the one it
+ * replaces (218 us against 185.5 us for quantize + up-proj + inter-layer),
+ * so the library's own MLP step keeps w8a8_gelu_quantize_act.
+ */
+int w8a8_gemm_dequant_gelu_amax(const int8_t* q_x, const float* s_x, const int8_t* w_q,
+                                const float* s_w, const void* bias_bf16, int64_t M, int64_t N,
+                                int64_t K, void* h_bf16, uint32_t* amax, void* stream);
+int w8a8_quantize_act_amax(const void* h_bf16, int64_t M, int64_t K, int64_t ldh,
+                           const uint32_t* amax, int8_t* q, int64_t ldq, float* scale,
+                           void* stream);
+
+/*
  * GEMM kernel configurations (tile shapes), chosen per GEMM shape -- the
  * Abstract's per-shape autotuning, here a fixed table built from measurement.
  */

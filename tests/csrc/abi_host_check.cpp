@@ -58,6 +58,21 @@ hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t) {
   ++g_rows;
   return hipSuccess;
 }
+int g_gelu_gemm = 0, g_quant_amax = 0;
+bool gemm_gelu_amax_supported(const GemmArgs& a) { return a.M % 256 == 0 && a.N % 256 == 0 && a.K % 64 == 0 && a.K >= 256; }
+hipError_t launch_gemm_gelu_amax(const GemmArgs& a, hipStream_t) {
+  CHECK(a.amax != nullptr && a.out != nullptr);
+  ++g_gelu_gemm;
+  return hipSuccess;
+}
+hipError_t launch_quantize_with_amax(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                     const uint32_t* amax, int8_t* q, int64_t ldq, float* scale,
+                                     hipStream_t) {
+  CHECK(x != nullptr && M >= 1 && K <= 12288 && ldx >= K && amax != nullptr && q != nullptr && ldq >= K &&
+        scale != nullptr);
+  ++g_quant_amax;
+  return hipSuccess;
+}
 int gemm_fp8_num_configs() { return 6; }
 const char* gemm_fp8_config_name(int c) { return (c >= 0 && c < 6) ? "stub" : nullptr; }
 int gemm_fp8_select_config(int64_t, int64_t, int64_t) { return 4; }
@@ -186,6 +201,28 @@ int main() {
   CHECK(w8a8_linear_fp8(x.data(), w8, sw.data(), nullptr, M, N, K, y.data(), ws_buf, 16, nullptr) ==
         W8A8_ERR_WORKSPACE);
   CHECK(g_gemm_fp8 == 2 && g_quant == 9);
+
+  // GELU-epilogue GEMM and the absmax-given quantizer (the inter-layer fusion variant)
+  {
+    const int64_t Mg = 256, Ng = 256, Kg = 256;
+    std::vector<int8_t> qg(Mg * Kg), wg(Ng * Kg);
+    std::vector<float> sxg(Mg), swg(Ng);
+    std::vector<uint16_t> hg(Mg * Ng);
+    std::vector<uint32_t> am(Mg);
+    CHECK(w8a8_gemm_dequant_gelu_amax(qg.data(), sxg.data(), wg.data(), swg.data(), nullptr, Mg, Ng, Kg,
+                                      hg.data(), am.data(), nullptr) == W8A8_OK);
+    CHECK(w8a8::g_gelu_gemm == 1);
+    CHECK(w8a8_gemm_dequant_gelu_amax(qg.data(), sxg.data(), wg.data(), swg.data(), nullptr, Mg, Ng, Kg,
+                                      hg.data(), nullptr, nullptr) == W8A8_ERR_NULL);
+    CHECK(w8a8_gemm_dequant_gelu_amax(qg.data(), sxg.data(), wg.data(), swg.data(), nullptr, 128, Ng, Kg,
+                                      hg.data(), am.data(), nullptr) == W8A8_ERR_SHAPE);
+    CHECK(w8a8::g_gelu_gemm == 1);
+    CHECK(w8a8_quantize_act_amax(hg.data(), Mg, Ng, Ng, am.data(), qg.data(), Ng, sxg.data(), nullptr) ==
+          W8A8_OK);
+    CHECK(w8a8_quantize_act_amax(hg.data(), Mg, Ng, Ng, nullptr, qg.data(), Ng, sxg.data(), nullptr) ==
+          W8A8_ERR_NULL);
+    CHECK(w8a8::g_quant_amax == 1);
+  }
 
   // configuration tables
   CHECK(w8a8_gemm_num_configs() == 11 && w8a8_gemm_fp8_num_configs() == 6);

@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
         "w8a8_linear_workspace_bytes": ([I64, I64], ctypes.c_size_t),
         "w8a8_linear": ([P, P, P, P, I64, I64, I64, P, P, ctypes.c_size_t, P], I),
         "w8a8_linear_noalloc": ([P, P, P, P, I64, I64, I64, P, P], I),
+        "w8a8_gemm_dequant_gelu_amax": ([P, P, P, P, P, I64, I64, I64, P, P, P], I),
+        "w8a8_quantize_act_amax": ([P, I64, I64, I64, P, P, I64, P, P], I),
         "w8a8_linear_noalloc_max_bytes": ([], ctypes.c_size_t),
         "w8a8_gelu_quantize_act": ([P, I64, I64, I64, P, I64, P, P, P], I),
         "w8a8_gemm_num_configs": ([], I),
@@ -217,6 +219,46 @@ def w8a8_gemm_dequant(q_x, s_x, w_q, s_w, bias=None, out=None):
                                 _ptr(out), _stream(q_x.device))
     _check(rc, "w8a8_gemm_dequant")
     return out
+
+
+def w8a8_gemm_dequant_gelu_amax(q_x, s_x, w_q, s_w, bias=None, h_out=None, amax=None):
+    """The GEMM with GELU and the row maxima of |h| in its epilogue (the
+    inter-layer fusion variant): -> (h bf16 [M, N], amax int32 [M] holding
+    the fp32 bit patterns of max_n |h[m, n]|)."""
+    M, N, K = _gemm_inputs(q_x, w_q)
+    _vec(s_x, "s_x", torch.float32, M)
+    _vec(s_w, "s_w", torch.float32, N)
+    _vec(bias, "bias", torch.bfloat16, N)
+    h_out = torch.empty((M, N), dtype=torch.bfloat16, device=q_x.device) if h_out is None else h_out
+    amax = torch.empty((M,), dtype=torch.int32, device=q_x.device) if amax is None else amax
+    _need(h_out, "h_out", torch.bfloat16, 2)
+    _vec(amax, "amax", torch.int32, M)
+    _same_device(q_x, s_x, w_q, s_w, bias, h_out, amax)
+    if tuple(h_out.shape) != (M, N) or not h_out.is_contiguous():
+        raise ValueError("h_out must be a contiguous [M, N] bf16 tensor")
+    rc = _lib.w8a8_gemm_dequant_gelu_amax(_ptr(q_x), _ptr(s_x), _ptr(w_q), _ptr(s_w), _ptr(bias), M, N,
+                                          K, _ptr(h_out), _ptr(amax), _stream(q_x.device))
+    _check(rc, "w8a8_gemm_dequant_gelu_amax")
+    return h_out, amax
+
+
+def w8a8_quantize_act_amax(h, amax, q=None, scale=None):
+    """Per-token quantization of bf16 rows whose absmax is given (fp32 bits in
+    an int32 [M] tensor, from w8a8_gemm_dequant_gelu_amax) -> (q, scale)."""
+    _need(h, "h", torch.bfloat16, 2)
+    M, K = h.shape
+    _vec(amax, "amax", torch.int32, M)
+    q = torch.empty((M, K), dtype=torch.int8, device=h.device) if q is None else q
+    scale = torch.empty((M,), dtype=torch.float32, device=h.device) if scale is None else scale
+    _need(q, "q", torch.int8, 2)
+    _need(scale, "scale", torch.float32, 1)
+    _same_device(h, amax, q, scale)
+    if tuple(q.shape) != (M, K) or tuple(scale.shape) != (M,) or not scale.is_contiguous():
+        raise ValueError("output shapes do not match h")
+    rc = _lib.w8a8_quantize_act_amax(_ptr(h), M, K, _rows(h, "h"), _ptr(amax), _ptr(q), _rows(q, "q"),
+                                     _ptr(scale), _stream(h.device))
+    _check(rc, "w8a8_quantize_act_amax")
+    return q, scale
 
 
 def w8a8_gemm_ex(q_x, s_x, w_q, s_w, bias=None, out=None, out_int32=False, config=-1):

@@ -240,6 +240,44 @@ int w8a8_linear_noalloc(const void* x_bf16, const int8_t* w_q, const float* s_w,
 
 size_t w8a8_linear_noalloc_max_bytes(void) { return w8a8::kNoAllocScratchBytes; }
 
+int w8a8_gemm_dequant_gelu_amax(const int8_t* q_x, const float* s_x, const int8_t* w_q,
+                                const float* s_w, const void* bias_bf16, int64_t M, int64_t N,
+                                int64_t K, void* h_bf16, uint32_t* amax, void* stream) {
+  if (int rc = check_gemm(q_x, w_q, M, N, K, h_bf16)) return rc;
+  if (int rc = check_dequant(s_x, s_w, bias_bf16, M, N)) return rc;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (amax == nullptr) return W8A8_ERR_NULL;
+  if (!aligned(amax, 4)) return W8A8_ERR_ALIGN;
+  GemmArgs a;
+  a.qx = q_x;
+  a.qw = w_q;
+  a.sx = s_x;
+  a.sw = s_w;
+  a.bias = static_cast<const uint16_t*>(bias_bf16);
+  a.out = h_bf16;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.amax = amax;
+  if (!w8a8::gemm_gelu_amax_supported(a)) {
+    const bool shape_ok = M % 256 == 0 && N % 256 == 0 && K % 64 == 0 && K >= 256;
+    return shape_ok ? W8A8_ERR_ALIGN : W8A8_ERR_SHAPE;
+  }
+  return hip_status(w8a8::launch_gemm_gelu_amax(a, as_stream(stream)));
+}
+
+int w8a8_quantize_act_amax(const void* h_bf16, int64_t M, int64_t K, int64_t ldh,
+                           const uint32_t* amax, int8_t* q, int64_t ldq, float* scale,
+                           void* stream) {
+  if (int rc = check_rows(h_bf16, M, K, ldh, 2, q, ldq, scale)) return rc;
+  if (M == 0) return W8A8_OK;
+  if (K > 12288) return W8A8_ERR_SHAPE;
+  if (amax == nullptr) return W8A8_ERR_NULL;
+  if (!aligned(amax, 4)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_quantize_with_amax(h_bf16, M, K, ldh, amax, q, ldq, scale,
+                                                    as_stream(stream)));
+}
+
 int w8a8_quantize_act_fp8(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, uint8_t* q,
                           int64_t ldq, float* scale, void* stream) {
   int8_t* qb = reinterpret_cast<int8_t*>(q);

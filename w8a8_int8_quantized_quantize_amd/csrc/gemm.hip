@@ -510,13 +510,38 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t 
 // dequantized and written as 8-byte runs.
 // EPI: the tile's scales and bias were staged in LDS (stage_epilogue_vectors)
 // and are read from there; otherwise from global memory.
-template <class C, bool EPI = false>
+// The 65536-entry table of correctly rounded bf16 GELU values (written at
+// build time by gen_gelu_lut.py, the same table the GELU quantizer uses).
+// The kernels reference it by name in device code: a constant device array
+// like this one is not registered as a host-visible symbol, so its device
+// address cannot be asked of the runtime.
+__device__ const uint16_t kGeluTable[65536] __attribute__((aligned(16))) = {
+#include "gelu_lut.inc"
+};
+
+// GELU of 8 packed bf16 outputs through the table (global memory,
+// L2-resident): one gather each.
+__device__ __forceinline__ uint4 gelu8(uint4 o) {
+  const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+  uint32_t h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    h[i] = static_cast<uint32_t>(kGeluTable[w[i] & 0xFFFFu]) |
+           (static_cast<uint32_t>(kGeluTable[w[i] >> 16]) << 16);
+  return make_uint4(h[0], h[1], h[2], h[3]);
+}
+
+// GELU: instead of y, store h = bf16(gelu(y)) (kGeluTable) and raise a.amax[m]
+// (fp32 bits of max |h| over the row; atomic max, exact in any order) to
+// each row's largest |h| over this wave's columns.  16x16 tiles only.
+template <class C, bool EPI = false, bool GELU = false>
 __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int64_t n0, int wn,
                                               int wm, int lane,
                                               const typename C::Acc (&acc)[C::FN][C::FM],
                                               const int8_t* smem = nullptr) {
   constexpr int MF = C::MF;
   constexpr int G = C::Op::kGroups;
+  static_assert(!GELU || (MF == 16 && C::FM % 2 == 0), "GELU epilogue: 16x16 blocks");
   const int lr = lane % MF, lq = lane / MF;
   // opaque bases: the scale / bias loads below must not be hoisted above the
   // K loop, where their ~100 registers would crowd out the loop's
@@ -587,16 +612,30 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
     // columns 8 (r >> 1) .. +7 of the block, in one 16-byte store.
 #pragma unroll
     for (int fj = 0; fj < C::FM; fj += 2) {
+      u16x2 hmax = {0, 0};
 #pragma unroll
       for (int fi = 0; fi < C::FN; ++fi) {
         __builtin_amdgcn_sched_barrier(0);
         const uint2 pa = pack(fi, fj, 0), pb = pack(fi, fj + 1, 0);
         const auto sx2 = __builtin_amdgcn_permlane16_swap(pa.x, pb.x, false, false);
         const auto sy2 = __builtin_amdgcn_permlane16_swap(pa.y, pb.y, false, false);
-        const uint4 o = make_uint4(sx2[0], sy2[0], sx2[1], sy2[1]);
+        uint4 o = make_uint4(sx2[0], sy2[0], sx2[1], sy2[1]);
         const int64_t m = m0 + wm * C::TM + (fj + (lq & 1)) * MF + lr;
         const int64_t n = n0 + wn * C::TN + fi * MF + (lq >> 1) * 8;
+        if constexpr (GELU) {
+          o = gelu8(o);
+          hmax = absmax2(absmax2(absmax2(absmax2(hmax, o.x), o.y), o.z), o.w);
+        }
         *reinterpret_cast<uint4*>(y + m * a.N + n) = o;
+      }
+      if constexpr (GELU) {
+        // lanes l and l ^ 32 hold the two column halves of the same row
+        float hm = absmax_of(hmax);
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        if (lq < 2) {
+          const int64_t m = m0 + wm * C::TM + (fj + (lq & 1)) * MF + lr;
+          atomicMax(a.amax + m, __float_as_uint(hm));
+        }
       }
     }
     return;
@@ -1217,7 +1256,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
 // stage after the workgroup's last tile.  The epilogue vectors (scales, bias)
 // alternate between two LDS buffers from tile to tile: group 0 loads the next
 // tile's while group 1 may still read the previous ones.
-template <class C, bool OUT_I32>
+template <class C, bool OUT_I32, bool GELU = false>
 __global__ __launch_bounds__(C::kThreads) void gemm_pp_kernel(GemmArgs a, int T, int MTi, int NTi) {
   static_assert(C::kWaves == 8 && C::WM == 2 && C::WN == 4 && C::kSteps == 1 && C::kSpread,
                 "ping-pong tiles: 2 x 4 waves, one k-step per stage, 3+ stages");
@@ -1326,7 +1365,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_pp_kernel(GemmArgs a, int T,
     if constexpr (OUT_I32)
       epilogue<C, true, false>(a, m0, n0, wv2 % C::WN, wv2 / C::WN, ln2, acc);
     else
-      epilogue_fast<C, EPI>(a, m0, n0, wv2 % C::WN, wv2 / C::WN, ln2, acc, epi);
+      epilogue_fast<C, EPI, GELU>(a, m0, n0, wv2 % C::WN, wv2 / C::WN, ln2, acc, epi);
     stored = true;
     par ^= 1;
     if (!more) break;
@@ -2032,6 +2071,42 @@ hipError_t launch_gemm_fp8(const GemmArgs& a, int cfg, hipStream_t stream) {
     case 5: return launch_cfg<F4, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+namespace {
+__global__ __launch_bounds__(256) void zero_u32(uint32_t* p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = 0u;
+}
+}  // namespace
+
+// The up-projection with GELU and the row absmax in its epilogue: the
+// ping-pong tile on interior tiles only (M, N multiples of 256, K a multiple
+// of 64 with at least 4 stages, aligned vectors).
+bool gemm_gelu_amax_supported(const GemmArgs& a) {
+  using C = C11;
+  return a.M % C::BM == 0 && a.N % C::BN == 0 && a.K % C::BK == 0 && a.K / C::BK >= C::STAGES &&
+         a.M > 0 && a.N > 0 && reinterpret_cast<uintptr_t>(a.sw) % 16 == 0 &&
+         reinterpret_cast<uintptr_t>(a.sx) % 16 == 0 && reinterpret_cast<uintptr_t>(a.bias) % 16 == 0;
+}
+
+hipError_t launch_gemm_gelu_amax(const GemmArgs& a, hipStream_t stream) {
+  using C = C11;
+  if (!gemm_gelu_amax_supported(a) || a.amax == nullptr) return hipErrorInvalidValue;
+  // the row maxima start from zero (|h| >= 0): a fill kernel, graph-capturable
+  const int64_t zb = std::min<int64_t>((a.M + 255) / 256, 1024);
+  zero_u32<<<dim3(static_cast<unsigned>(zb)), dim3(256), 0, stream>>>(a.amax, a.M);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t MTi = a.M / C::BM, NTi = a.N / C::BN, Ti = MTi * NTi;
+  if (Ti > INT32_MAX) return hipErrorInvalidValue;
+  int grid = 0;
+  e = persistent_grid<gemm_pp_kernel<C, false, true>>(C::kThreads, Ti, grid);
+  if (e != hipSuccess) return e;
+  gemm_pp_kernel<C, false, true><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
+      a, static_cast<int>(Ti), static_cast<int>(MTi), static_cast<int>(NTi));
+  return hipGetLastError();
 }
 
 // The single-launch fused linear takes M <= 16 rows whose K fits one chunk

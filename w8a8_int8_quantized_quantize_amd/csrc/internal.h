@@ -28,6 +28,9 @@ struct GemmArgs {
   const uint16_t* bias;  // [N] bf16 or nullptr
   void* out;          // [M, N] bf16 or int32
   int64_t M, N, K;
+  // GELU epilogue variant only (launch_gemm_gelu_amax): the [M] row maxima
+  // of |h| (fp32 bit patterns)
+  uint32_t* amax = nullptr;
 };
 
 // The fused linear for a handful of token rows in one launch (quantize +
@@ -44,6 +47,17 @@ struct RowsArgs {
 };
 bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t stream);
+
+// The GEMM whose epilogue also applies GELU and raises the row maxima of |h|
+// (the inter-layer fusion variant): out = h = bf16(gelu(y)) [M, N] bf16,
+// amax[m] = max |h[m, :]| (fp32 bits; zeroed first).  Interior shapes only.
+bool gemm_gelu_amax_supported(const GemmArgs& a);
+hipError_t launch_gemm_gelu_amax(const GemmArgs& a, hipStream_t stream);
+// Per-token quantization of bf16 rows whose absmax is already known
+// (amax[m]: fp32 bits): the same codes and scales as launch_quantize_rows.
+hipError_t launch_quantize_with_amax(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                     const uint32_t* amax, int8_t* q, int64_t ldq, float* scale,
+                                     hipStream_t stream);
 
 int gemm_num_configs();
 const char* gemm_config_name(int cfg);

@@ -43,6 +43,8 @@
 #include "internal.h"
 #include "quant_codes.h"
 
+#include <atomic>
+
 namespace w8a8 {
 namespace {
 
@@ -247,6 +249,36 @@ __global__ __launch_bounds__(kThreads) void quantize_bf16_loop(
       at(dst, c) = mode == 2 ? codes_bf16x8<2, FP8>(v, s, r)
                              : (mode == 1 ? codes_bf16x8<1, FP8>(v, s, r) : make_uint2(0u, 0u));
     }
+  }
+}
+
+// Rows whose absmax is known (amax[row]: fp32 bits), e.g. raised by the
+// GEMM's GELU epilogue: the same scale and codes as quantize_bf16_regs on
+// the same row (its absmax is the same value), without the reduction.
+template <int CH>
+__global__ __launch_bounds__(kThreads) void quantize_bf16_amax_regs(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+    const uint32_t* __restrict__ amax, int8_t* __restrict__ q, int64_t ldq,
+    float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  for (int64_t row = (int64_t)blockIdx.x * kWaves + wave_id(); row < M;
+       row += (int64_t)gridDim.x * kWaves) {
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    uint4 raw[CH];
+    load_row<CH>(reinterpret_cast<const uint4*>(x + row * ldx), nch, ln, raw);
+    const float s = __uint_as_float(amax[row]) / 127.0f;
+    float r = 0.0f;
+    int mode = 0;
+    if (s >= kFastMinScale) {
+      r = 1.0f / s;
+      mode = 2;
+    } else if (s != 0.0f) {
+      mode = 1;
+    }
+    if (lane == 0) scale[row] = s;
+    emit_bf16_row<CH, false>(raw, mode, s, r, nch, ln, q + row * ldq);
   }
 }
 
@@ -558,6 +590,24 @@ hipError_t launch_f32(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t*
 #undef W8A8_FOR_CH
 
 }  // namespace
+
+hipError_t launch_quantize_with_amax(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                     const uint32_t* amax, int8_t* q, int64_t ldq, float* scale,
+                                     hipStream_t stream) {
+  const int64_t per_lane = (K / 8 + 63) / 64;
+  const int64_t blocks = std::min<int64_t>((M + kWaves - 1) / kWaves, kMaxBlocks);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+#define W8A8_A_CASE(CHV)                                                                        \
+  if (K > 0 && per_lane <= CHV) {                                                               \
+    quantize_bf16_amax_regs<CHV><<<grid, block, 0, stream>>>(xb, M, K, ldx, amax, q, ldq, scale); \
+    return hipGetLastError();                                                                   \
+  }
+  W8A8_A_CASE(1) W8A8_A_CASE(2) W8A8_A_CASE(3) W8A8_A_CASE(4) W8A8_A_CASE(6) W8A8_A_CASE(8)
+  W8A8_A_CASE(12) W8A8_A_CASE(16) W8A8_A_CASE(24)
+#undef W8A8_A_CASE
+  return hipErrorInvalidValue;  // rows longer than 24 chunks per lane (K > 12288)
+}
 
 hipError_t launch_quantize_rows(QuantSrc src, const void* x, int64_t M, int64_t K, int64_t ldx,
                                 int8_t* q, int64_t ldq, float* scale, uint16_t* h_out,
