@@ -1380,56 +1380,89 @@ __global__ __launch_bounds__(C::kThreads) void gemm_pp_kernel(GemmArgs a, int T,
 // ----------------------------------------------------------- few tokens --
 // A GEMM with a handful of token rows is bound by streaming the weights from
 // HBM once (M = 1 .. 16: 2 .. 32 ops per weight byte).  Each workgroup owns
-// NB blocks of 16 output columns and 16 token rows; its NW waves split K,
-// each loading its weight and activation fragments straight into registers
-// (ST 64-byte K steps in flight per wave, no LDS staging), accumulating with
-// v_mfma_i32_16x16x64_i8, then the waves' partial sums meet in LDS and the
-// first wave runs the epilogue.  grid.y covers M in steps of 16, so any M
-// works (larger M is better served by the tiled kernel).
+// NB blocks of 16 output columns and MB blocks of 16 token rows; its NW waves
+// split K, each loading its weight and activation fragments straight into
+// registers (ST 64-byte K steps in flight per wave, no LDS staging),
+// accumulating with v_mfma_i32_16x16x64_i8, then the waves' partial sums
+// meet in LDS and the MB x NB result blocks are shared out over the waves
+// for the reduction and the epilogue.  The int8 configurations load
+// coalesced (COAL, below) and permute into the MFMA layout: a load in that
+// layout puts four different rows under every four consecutive lanes, and
+// it measured 5-9% slower on the weight-streaming shapes (1 and 16 rows)
+// and 1.8x slower at 256 rows than the coalesced load plus the permute.  grid.y covers M in steps of 16 MB, so
+// any M works.  MB = 1 is the few-row kernel proper; MB = 4 (64 rows) serves
+// a few hundred tokens, where the tiled kernel's large tiles would leave
+// most CUs idle: 64 x 48 blocks make 256 workgroups of a 256 x 3072 output.
 //   MFMA 16x16x64 layout: lane l holds row l % 16 of a 16-row operand, K
 //   bytes 16 (l / 16) .. +15 of a 64-byte step; D[i][j] (i: weight row n,
 //   j: token m) sits in lane j + 16 (i / 4), register i % 4.
 //   FP8 operands: v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales), a
 //   128-byte K step, lane l holding 32 bytes (two 16-byte loads) of row l % 16
 //   at K bytes 32 (l / 16) .. +31, fp32 accumulators, same result layout.
-template <int NW, int NB, bool OUT_I32, int ST, bool LOOP, bool FP8 = false>
+// A 16-byte fragment moved between lanes: lane d receives the fragment of
+// lane perm / 4 (perm: byte address as ds_bpermute takes it).
+__device__ __forceinline__ v4i to_mfma_layout(v4i v, int perm) {
+  v4i o;
+  o[0] = __builtin_amdgcn_ds_bpermute(perm, v[0]);
+  o[1] = __builtin_amdgcn_ds_bpermute(perm, v[1]);
+  o[2] = __builtin_amdgcn_ds_bpermute(perm, v[2]);
+  o[3] = __builtin_amdgcn_ds_bpermute(perm, v[3]);
+  return o;
+}
+template <class F>
+__device__ __forceinline__ F to_mfma_layout(F v, int) {
+  return v;  // FP8 fragments keep the MFMA layout (no coalesced variant)
+}
+
+template <int NW, int NB, bool OUT_I32, int ST, bool LOOP, bool FP8 = false, int MB = 1,
+          bool COAL = false>
 __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
   static_assert(!(FP8 && OUT_I32), "FP8 products accumulate in fp32: bf16 output only");
+  static_assert(!(FP8 && COAL), "coalesced loads: int8 operands");
   using Frag = std::conditional_t<FP8, v8i, v4i>;
   using Acc = std::conditional_t<FP8, v4f, v4i>;
   constexpr int SB = FP8 ? 128 : 64;  // K bytes of one MFMA
   constexpr int PB = SB / 4;          // K bytes one lane supplies per step
-  __shared__ Acc part[NW][NB][64];
+  constexpr int NBLK = MB * NB;       // result blocks of the workgroup
+  __shared__ Acc part[NW][NBLK][64];
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int64_t M = a.M, N = a.N, K = a.K;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16 * NB;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16 * MB;
   const int r = lane % 16, kq = lane / 16;
+  // COAL: each lane loads row lane / 4, piece lane % 4 (four consecutive lanes
+  // read one 64-byte run of a row, so a load instruction touches 16 cache
+  // lines rather than 64), and a ds_bpermute then moves every fragment into
+  // the MFMA layout above (lane d takes lane 4 (d % 16) + d / 16's piece)
+  const int lr = COAL ? lane / 4 : r, lq = COAL ? lane % 4 : kq;
+  const int perm = 4 * (4 * (lane % 16) + lane / 16);  // bpermute byte address
   const int64_t steps = (K + SB - 1) / SB;
   const int64_t per = (steps + NW - 1) / NW;
   const int64_t s0 = wave * per, s1 = min(steps, s0 + per);
-  const int64_t mr = m0 + r;
-  const bool mrow = mr < M;
-  const int8_t* xrow = a.qx + (mrow ? mr : 0) * K;
+  const int8_t* xrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t mr = m0 + 16 * mb + lr;
+    xrow[mb] = a.qx + (mr < M ? mr : 0) * K;
+  }
   const int8_t* wrow[NB];
-  bool nrow[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int64_t nr = n0 + 16 * b + r;
-    nrow[b] = nr < N;
-    wrow[b] = a.qw + (nrow[b] ? nr : 0) * K;
+    const int64_t nr = n0 + 16 * b + lr;
+    wrow[b] = a.qw + (nr < N ? nr : 0) * K;
   }
   // The epilogue's scales and biases are loaded first, so that their latency
   // hides behind the weight stream instead of following it.
   // (Indices are clamped rather than tested, so that the loads are
   // unconditional and all go out before the first wait.)
-  float sxe = 0.0f, swe[NB][4];
+  float sxe[MB], swe[NB][4];
   uint32_t braw[NB][4];  // bf16 bias bits, widened in the epilogue
-  // (Every wave loads them, though only wave 0 uses them: a branch here
-  // would make the waits after it conservative.)
+  // (Every wave loads them all, though each uses only its own blocks': a
+  // branch here would make the waits after it conservative.)
   if constexpr (!OUT_I32) {
-    sxe = a.sx[min(m0 + lane % 16, M - 1)];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) sxe[mb] = a.sx[min(m0 + 16 * mb + lane % 16, M - 1)];
     // no bias: read any valid 16-bit word, replaced by -0.0 in the epilogue
     const uint16_t* bsrc = a.bias ? a.bias : reinterpret_cast<const uint16_t*>(a.sw);
 #pragma unroll
@@ -1441,9 +1474,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
         braw[b][e] = bsrc[n];
       }
   }
-  Acc acc[NB];
+  Acc acc[MB][NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = Acc{};
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[mb][b] = Acc{};
   // one lane's operand at K byte k of a row (kc2: its second 16-byte piece,
   // clamped into the row when it lies past K)
   auto load_op = [&](const int8_t* row, int64_t kc, int64_t kc2) {
@@ -1457,18 +1492,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
     }
   };
   auto chunk = [&](int64_t c0) {
-    Frag xf[ST], wf[ST][NB];
+    Frag xf[ST][MB], wf[ST][NB];
     // Loads only (addresses clamped into the operands): a test on loaded
     // data here would make each load wait for the one before.  Rows beyond
     // M or N only feed outputs that are never stored, so they need no
     // zeroing; steps past the wave's share are skipped below.
 #pragma unroll
     for (int i = 0; i < ST; ++i) {
-      const int64_t k = (c0 + i) * SB + kq * PB;
+      const int64_t k = (c0 + i) * SB + lq * PB;  // this lane's load
       const bool in = (c0 + i) < s1 && k < K;
       const int64_t kc = in ? k : 0;
       const int64_t kc2 = (in && k + 16 < K) ? k + 16 : kc;
-      xf[i] = load_op(xrow, kc, kc2);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) xf[i][mb] = load_op(xrow[mb], kc, kc2);
 #pragma unroll
       for (int b = 0; b < NB; ++b) wf[i][b] = load_op(wrow[b], kc, kc2);
       __builtin_amdgcn_sched_barrier(0);  // issue order = step order
@@ -1479,19 +1515,28 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
     for (int i = 0; i < ST; ++i) {
       if (c0 + i >= s1) break;  // wave-uniform
       // the 16-byte pieces of a step past K (K not a multiple of SB) are zeroed
-      const int64_t k = (c0 + i) * SB + kq * PB;
-      Frag xv = xf[i];
-      if (!(k < K)) xv = Frag{};
-      if constexpr (FP8) {
-        if (!(k + 16 < K)) xv = __builtin_shufflevector(xv, Frag{}, 0, 1, 2, 3, 12, 13, 14, 15);
+      const int64_t k = (c0 + i) * SB + kq * PB;  // the piece this lane multiplies
+      if constexpr (COAL) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) xf[i][mb] = to_mfma_layout(xf[i][mb], perm);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wf[i][b] = to_mfma_layout(wf[i][b], perm);
       }
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        if constexpr (FP8)
-          acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i][b], xv, acc[b], 0, 0, 0,
-                                                                     127, 0, 127);
-        else
-          acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i][b], xv, acc[b], 0, 0, 0);
+      for (int mb = 0; mb < MB; ++mb) {
+        Frag xv = xf[i][mb];
+        if (!(k < K)) xv = Frag{};
+        if constexpr (FP8) {
+          if (!(k + 16 < K)) xv = __builtin_shufflevector(xv, Frag{}, 0, 1, 2, 3, 12, 13, 14, 15);
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          if constexpr (FP8)
+            acc[mb][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i][b], xv, acc[mb][b], 0,
+                                                                         0, 0, 127, 0, 127);
+          else
+            acc[mb][b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i][b], xv, acc[mb][b], 0, 0, 0);
+        }
       }
     }
   };
@@ -1505,17 +1550,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
     if (s0 < s1) chunk(s0);
   }
 #pragma unroll
-  for (int b = 0; b < NB; ++b) part[wave][b][lane] = acc[b];
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) part[wave][mb * NB + b][lane] = acc[mb][b];
   __syncthreads();
-  if (wave != 0) return;
-  const int64_t m = m0 + lane % 16;
-  if (m >= M) return;
+  // result block j (row block j / NB, column block j % NB) goes to wave j % NW
   const int nq = 4 * (lane / 16);
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    Acc t = part[0][b][lane];
+  for (int j = 0; j < NBLK; ++j) {
+    if (j % NW != wave) continue;  // wave-uniform
+    const int mb = j / NB, b = j % NB;
+    const int64_t m = m0 + 16 * mb + lane % 16;
+    if (m >= M) continue;
+    Acc t = part[0][j][lane];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) t += part[w][b][lane];
+    for (int w = 1; w < NW; ++w) t += part[w][j][lane];
     const int64_t nb = n0 + 16 * b + nq;
     if constexpr (OUT_I32) {
       int32_t* out = static_cast<int32_t*>(a.out) + m * N + nb;
@@ -1528,7 +1577,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float bv = a.bias ? __uint_as_float(braw[b][e] << 16) : -0.0f;
-        v[e] = dequant(t[e], sxe, swe[b][e], bv);
+        v[e] = dequant(t[e], sxe[mb], swe[b][e], bv);
       }
       if (N % 4 == 0 && nb + 3 < N) {
         // the lane's 4 columns in one 8-byte store (rows start 8-byte aligned)
@@ -1611,12 +1660,15 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   // the weight fragments of this wave's K share (past the share or past K:
-  // clamped to offset 0, never used)
-  const int8_t* wrow = a.qw + min(n0 + r, N - 1) * K;
+  // clamped to offset 0, never used), loaded four lanes to a 64-byte run of
+  // a row (lane l: row l / 4, piece l % 4) and moved into the MFMA layout by
+  // a ds_bpermute before use (lane d takes lane 4 (d % 16) + d / 16's piece)
+  const int8_t* wrow = a.qw + min(n0 + lane / 4, N - 1) * K;
+  const int perm = 4 * (4 * (lane % 16) + lane / 16);
   v4i wf[ST];
 #pragma unroll
   for (int i = 0; i < ST; ++i) {
-    const int64_t k = (s0 + i) * 64 + kq * 16;
+    const int64_t k = (s0 + i) * 64 + (lane % 4) * 16;
     const int64_t kc = ((s0 + i) < s1 && k < K) ? k : 0;
     wf[i] = *reinterpret_cast<const v4i*>(wrow + kc);
     __builtin_amdgcn_sched_barrier(0);
@@ -1686,7 +1738,7 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
     const int64_t k = (s0 + i) * 64 + kq * 16;
     v4i xq = {0, 0, 0, 0};
     if (k < K) xq = *reinterpret_cast<const v4i*>(crow_l + k);
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(wf[i], xq, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(to_mfma_layout(wf[i], perm), xq, acc, 0, 0, 0);
   }
   part[wave][lane] = acc;
   __syncthreads();
@@ -1712,30 +1764,33 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
   }
 }
 
-template <int NW, int NB, bool I32, int ST, bool LOOP = false, bool FP8 = false>
+template <int NW, int NB, bool I32, int ST, bool LOOP = false, bool FP8 = false, int MB = 1,
+          bool COAL = false>
 hipError_t launch_few_rows_st(const GemmArgs& a, hipStream_t stream) {
-  const int64_t gx = (a.N + 16 * NB - 1) / (16 * NB), gy = (a.M + 15) / 16;
+  const int64_t gx = (a.N + 16 * NB - 1) / (16 * NB), gy = (a.M + 16 * MB - 1) / (16 * MB);
   if (gx > INT32_MAX || gy > 65535) return hipErrorInvalidValue;
-  gemm_few_rows<NW, NB, I32, ST, LOOP, FP8>
+  gemm_few_rows<NW, NB, I32, ST, LOOP, FP8, MB, COAL>
       <<<dim3(static_cast<unsigned>(gx), static_cast<unsigned>(gy)), dim3(64 * NW), 0, stream>>>(a);
   return hipGetLastError();
 }
 
-// Steps in flight per wave: the smallest of 1, 2, 3, 4, 6, 8, 12 that covers
-// the wave's share of K (no load is wasted on a step past the share), else
-// a loop of 12-step chunks.
-template <int NW, int NB, bool I32, bool FP8 = false>
+// Steps in flight per wave: the smallest of 1, 2, 3, 4, 6, 8, 12 (at most
+// STMAX, which bounds the fragment registers) that covers the wave's share
+// of K (no load is wasted on a step past the share), else a loop of
+// STLOOP-step chunks (the loop's own registers leave room for fewer).
+template <int NW, int NB, bool I32, bool FP8 = false, int MB = 1, int STMAX = 12,
+          int STLOOP = STMAX, bool COAL = false>
 hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
   constexpr int64_t SB = FP8 ? 128 : 64;
   const int64_t per = ((a.K + SB - 1) / SB + NW - 1) / NW;
-  if (per <= 1) return launch_few_rows_st<NW, NB, I32, 1, false, FP8>(a, stream);
-  if (per <= 2) return launch_few_rows_st<NW, NB, I32, 2, false, FP8>(a, stream);
-  if (per <= 3) return launch_few_rows_st<NW, NB, I32, 3, false, FP8>(a, stream);
-  if (per <= 4) return launch_few_rows_st<NW, NB, I32, 4, false, FP8>(a, stream);
-  if (per <= 6) return launch_few_rows_st<NW, NB, I32, 6, false, FP8>(a, stream);
-  if (per <= 8) return launch_few_rows_st<NW, NB, I32, 8, false, FP8>(a, stream);
-  if (per <= 12) return launch_few_rows_st<NW, NB, I32, 12, false, FP8>(a, stream);
-  return launch_few_rows_st<NW, NB, I32, 12, true, FP8>(a, stream);
+#define W8A8_ST_CASE(STV)                                                                   \
+  if constexpr (STV <= STMAX) {                                                             \
+    if (per <= STV) return launch_few_rows_st<NW, NB, I32, STV, false, FP8, MB, COAL>(a, stream); \
+  }
+  W8A8_ST_CASE(1) W8A8_ST_CASE(2) W8A8_ST_CASE(3) W8A8_ST_CASE(4) W8A8_ST_CASE(6)
+  W8A8_ST_CASE(8) W8A8_ST_CASE(12)
+#undef W8A8_ST_CASE
+  return launch_few_rows_st<NW, NB, I32, STLOOP, true, FP8, MB, COAL>(a, stream);
 }
 
 template <int CH, int ST>
@@ -1758,7 +1813,8 @@ hipError_t launch_linear_few_rows_ch(const RowsArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_few_rows_any(const GemmArgs& a, bool i32, hipStream_t stream) {
-  return i32 ? launch_few_rows<4, 1, true>(a, stream) : launch_few_rows<4, 1, false>(a, stream);
+  return i32 ? launch_few_rows<4, 1, true, false, 1, 12, 12, true>(a, stream)
+             : launch_few_rows<4, 1, false, false, 1, 12, 12, true>(a, stream);
 }
 
 // ------------------------------------------------------- configurations --
@@ -1784,6 +1840,10 @@ using C11 = Tile<256, 256, 2, 4, 64, 4, 16>;  // C9 with 8 waves (2 per SIMD), w
 // configuration 12: C11's tile on the ping-pong kernel (gemm_pp_kernel) for
 // interior tiles; its edge tiles, and shapes with K < STAGES x BK, take C11's
 // own kernels
+// configuration 13: the split-K register kernel (gemm_few_rows) with blocks
+// of 64 token rows and 48 columns, for a few hundred tokens: 256 workgroups
+// on a 256 x 3072 output, where the tiled kernels' large tiles would leave
+// most CUs idle
 
 const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 0.97f},
@@ -1799,10 +1859,12 @@ const ConfigInfo kConfigs[] = {
     {"bm256_bn192_bk64_s4_mf16", 256, 192, 256, 1, 0.93f},
     {"bm256_bn256_bk64_s4_mf16_w8", 256, 256, 512, 1, 0.99f},
     {"bm256_bn256_bk64_s4_mf16_pp", 256, 256, 512, 1, 1.05f},
+    {"rows64_bn48_splitk8_mf16", 64, 48, 512, 1, 0.30f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kSkinny = 6;    // 16-row tiled kernel
 constexpr int kFewRows = 8;   // split-K few-row kernel
+constexpr int kRowBlocks = 13;  // split-K kernel on 64-row blocks
 constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
 // Persistent grid: as many workgroups of `kernel` as fit on the device at
@@ -1954,7 +2016,7 @@ const MeasuredChoice kMeasured[] = {
     {16, 18432, 3072, 8},
     {16, 3072, 3072, 8},
     {256, 18432, 3072, 2},     // bm256_bn128_bk128_s3_mf32
-    {256, 3072, 3072, 5},      // bm64_bn64_bk128_s2_mf32
+    {256, 3072, 3072, 13},     // rows64_bn48_splitk8_mf16
     {4608, 9216, 3072, 12},    // 1024px block chain, all four GEMMs: the ping-pong tile
     {4608, 3072, 3072, 12},
     {4608, 12288, 3072, 12},
@@ -1992,6 +2054,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   double best_cost = 1e300;
   for (int c = 0; c < kNumConfigs; ++c) {
     if (c == kSkinny || c == kFewRows) continue;  // chosen above for M <= 16
+    if (c == kRowBlocks) continue;  // measured choice only
     const ConfigInfo& ci = kConfigs[c];
     const int64_t tiles = ((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
     // workgroups resident on one CU share its matrix-core throughput
@@ -2146,6 +2209,8 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 10: return launch_cfg_out<C10>(a, out_int32, stream);
     case 11: return launch_cfg_out<C11>(a, out_int32, stream);
     case 12: return out_int32 ? launch_pp<C11, true>(a, stream) : launch_pp<C11, false>(a, stream);
+    case 13: return out_int32 ? launch_few_rows<8, 3, true, false, 4, 6, 4, true>(a, stream)
+                              : launch_few_rows<8, 3, false, false, 4, 6, 4, true>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
