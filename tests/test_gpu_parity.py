@@ -228,6 +228,45 @@ def test_consecutive_interior_tiles_every_config(M, N, K):
         assert np.array_equal(bits(yc), yo), w8.w8a8_gemm_config_name(c)
 
 
+def _at_offset(t: torch.Tensor, k: int) -> torch.Tensor:
+    """A copy of 1-D t that starts k elements into a fresh allocation."""
+    big = torch.zeros(t.numel() + k, dtype=t.dtype, device=DEV)
+    big[k:] = t
+    return big[k:]
+
+
+# Scale and bias vectors at offsets the ABI accepts but the vector epilogue
+# cannot take (s_x, s_w 4 bytes past a 16-byte boundary, bias 2 bytes): the
+# interior tiles then read them element by element (and the 256 x 256
+# ping-pong configuration runs its 8-wave generic kernel).  Every int8
+# configuration bit-exact against the oracle, every FP8 one equal to its own
+# output with aligned vectors.
+@pytest.mark.parametrize("M,N,K", [(512, 768, 512), (600, 700, 1024)])
+def test_unaligned_scale_and_bias_vectors_every_config(M, N, K):
+    rng = np.random.default_rng(M + 3 * N + K)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0]
+    wd = torch.from_numpy(w).to(DEV)
+    wq, sw = w8.w8a8_quantize_weight(wd)
+    wqo, swo = oracle.quantize_rows_f32(w)
+    want = oracle.linear(xb, wqo, swo, bb)["y"]
+    x, bias = dev_bf16(xb), dev_bf16(bb)
+    q, s = w8.w8a8_quantize_act(x)
+    s1, sw1, b1 = _at_offset(s, 1), _at_offset(sw, 1), _at_offset(bias, 1)
+    assert s1.data_ptr() % 16 == 4 and sw1.data_ptr() % 16 == 4 and b1.data_ptr() % 16 == 2
+    for c in range(ncfg()):
+        yc = w8.w8a8_gemm_ex(q, s1, wq, sw1, b1, config=c)
+        assert np.array_equal(bits(yc), want), w8.w8a8_gemm_config_name(c)
+    qf, sf = w8.w8a8_quantize_act_fp8(x)
+    wf, swf = w8.w8a8_quantize_weight_fp8(wd)
+    sf1, swf1 = _at_offset(sf, 1), _at_offset(swf, 1)
+    for c in range(w8.w8a8_gemm_fp8_num_configs()):
+        ya = w8.w8a8_gemm_dequant_fp8(qf, sf, wf, swf, bias, config=c)
+        yu = w8.w8a8_gemm_dequant_fp8(qf, sf1, wf, swf1, b1, config=c)
+        assert torch.equal(ya, yu), w8.w8a8_gemm_fp8_config_name(c)
+
+
 def test_linear_k_zero_is_bias_and_empty_batches():
     N = 40
     rng = np.random.default_rng(5)

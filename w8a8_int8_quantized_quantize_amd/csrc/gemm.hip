@@ -503,13 +503,6 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int64_t m0, int64_t 
   }
 }
 
-// Interior-tile bf16 epilogue, stored straight from the MFMA layout.  All
-// scales and biases the lane needs are fetched up front with vector loads
-// (four consecutive columns per 16-byte s_w load and 8-byte bias load; both
-// vectors are aligned on this path), then each accumulator block is
-// dequantized and written as 8-byte runs.
-// EPI: the tile's scales and bias were staged in LDS (stage_epilogue_vectors)
-// and are read from there; otherwise from global memory.
 // The 65536-entry table of correctly rounded bf16 GELU values (written at
 // build time by gen_gelu_lut.py, the same table the GELU quantizer uses).
 // The kernels reference it by name in device code: a constant device array
@@ -531,10 +524,18 @@ __device__ __forceinline__ uint4 gelu8(uint4 o) {
   return make_uint4(h[0], h[1], h[2], h[3]);
 }
 
+// Interior-tile bf16 epilogue, stored straight from the MFMA layout.  All
+// scales and biases the lane needs are fetched up front (four consecutive
+// columns at a time), then each accumulator block is dequantized and
+// written as 8-byte runs.
+// EPI: the tile's scales and bias were staged in LDS (stage_epilogue_vectors)
+// and are read from there; otherwise from global memory, with 16-byte s_w
+// and 8-byte bias loads when VEC (the vectors are aligned for them), else
+// element by element (any alignment the ABI accepts).
 // GELU: instead of y, store h = bf16(gelu(y)) (kGeluTable) and raise a.amax[m]
 // (fp32 bits of max |h| over the row; atomic max, exact in any order) to
 // each row's largest |h| over this wave's columns.  16x16 tiles only.
-template <class C, bool EPI = false, bool GELU = false>
+template <class C, bool EPI = false, bool GELU = false, bool VEC = true>
 __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int64_t n0, int wn,
                                               int wm, int lane,
                                               const typename C::Acc (&acc)[C::FN][C::FM],
@@ -587,8 +588,15 @@ __device__ __forceinline__ void epilogue_fast(const GemmArgs& a, int64_t m0, int
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int64_t n = n0 + wn * C::TN + fi * MF + lq * 4 + g * 8;
-        sw[fi][g] = *reinterpret_cast<const float4*>(swp + n);
-        bb[fi][g] = bp ? *reinterpret_cast<const uint2*>(bp + n) : nobias;
+        if constexpr (VEC) {
+          sw[fi][g] = *reinterpret_cast<const float4*>(swp + n);
+          bb[fi][g] = bp ? *reinterpret_cast<const uint2*>(bp + n) : nobias;
+        } else {
+          sw[fi][g] = make_float4(swp[n], swp[n + 1], swp[n + 2], swp[n + 3]);
+          bb[fi][g] = bp ? make_uint2(bp[n] | (static_cast<uint32_t>(bp[n + 1]) << 16),
+                                      bp[n + 2] | (static_cast<uint32_t>(bp[n + 3]) << 16))
+                         : nobias;
+        }
       }
   }
   uint16_t* y = static_cast<uint16_t*>(a.out);
@@ -1098,13 +1106,13 @@ __device__ __forceinline__ void tile_mainloop(const GemmArgs& a, int8_t* smem, i
   }
 }
 
-template <class C, bool FAST, bool OUT_I32, bool EPI = false>
+template <class C, bool FAST, bool OUT_I32, bool EPI = false, bool VEC = true>
 __device__ __forceinline__ void tile_epilogue(const GemmArgs& a, int64_t m0, int64_t n0, int wave,
                                               int lane, const typename C::Acc (&acc)[C::FN][C::FM],
                                               const int8_t* smem = nullptr) {
   const int wn = wave % C::WN, wm = wave / C::WN;
   if constexpr (FAST && !OUT_I32)
-    epilogue_fast<C, EPI>(a, m0, n0, wn, wm, lane, acc, smem);
+    epilogue_fast<C, EPI, false, VEC>(a, m0, n0, wn, wm, lane, acc, smem);
   else
     epilogue<C, OUT_I32, !FAST>(a, m0, n0, wn, wm, lane, acc);
 }
@@ -1137,19 +1145,22 @@ __device__ __forceinline__ void edge_coords(int e, int MT, int NT, int MTi, int 
 // behind its arithmetic and stores.
 // Two kernels per configuration: the interior one (EDGE = false) takes the
 // MTi x NTi tiles that lie wholly inside M and N -- the host launches it only
-// when K is a whole number of stages, output rows are multiples of 16 bytes
-// and the scales / bias are vector aligned -- with unguarded loads, chained
-// tiles and the vector epilogue; the edge one takes the remaining tiles with
+// when K is a whole number of stages and output rows are multiples of 16
+// bytes -- with unguarded loads, chained tiles and the vector epilogue (its
+// VEC form when the scales / bias are vector aligned, else reading them
+// element by element); the edge one takes the remaining tiles with
 // clamped loads and guarded stores.  Kept apart, the interior kernel holds no
 // registers for the guarded code: it does not spill, so no reload (and no
 // wait for all outstanding loads that a reload implies) sits between a tile's
 // K loop and its epilogue while the next tile's first stages are in flight.
-template <class C, bool OUT_I32, bool EDGE>
+template <class C, bool OUT_I32, bool EDGE, bool VEC = true>
 __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, int MT, int NT,
                                                            int MTi, int NTi, int all) {
   constexpr bool FAST = !EDGE;
   // interior bf16 tiles of large configurations stage their epilogue vectors
-  constexpr bool EPI = FAST && !OUT_I32 && C::kEpiLds;
+  // (VEC: the vectors are aligned for it; otherwise the epilogue reads them
+  // from global memory element by element)
+  constexpr bool EPI = FAST && !OUT_I32 && C::kEpiLds && VEC;
   __shared__ __attribute__((aligned(1024))) int8_t smem[C::STAGES * C::kStage + (EPI ? C::kEpiBytes : 0)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1207,7 +1218,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
     }
     int ln2 = lane, wv2 = wave;
     asm volatile("" : "+v"(ln2), "+s"(wv2));
-    tile_epilogue<C, FAST, OUT_I32, EPI>(a, m0, n0, wv2, ln2, acc, smem);
+    tile_epilogue<C, FAST, OUT_I32, EPI, VEC>(a, m0, n0, wv2, ln2, acc, smem);
     // the next tile's first stages went out before these stores; the
     // interior bf16 epilogue issues exactly kFastStores of them
     stored = FAST && !OUT_I32;
@@ -1896,34 +1907,44 @@ hipError_t persistent_grid(int threads, int64_t tiles, int& grid) {
   return hipSuccess;
 }
 
+template <class C, bool I32, bool VEC>
+hipError_t launch_interior(const GemmArgs& a, int64_t Ti, int64_t MT, int64_t NT, int64_t MTi,
+                           int64_t NTi, hipStream_t stream) {
+  int grid = 0;
+  hipError_t e = persistent_grid<gemm_kernel<C, I32, false, VEC>>(C::kThreads, Ti, grid);
+  if (e != hipSuccess) return e;
+  gemm_kernel<C, I32, false, VEC><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
+      a, static_cast<int>(Ti), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),
+      static_cast<int>(NTi), 0);
+  return hipGetLastError();
+}
+
 template <class C, bool I32>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t MT = (a.M + C::BM - 1) / C::BM;
   const int64_t NT = (a.N + C::BN - 1) / C::BN;
   if (MT * NT > INT32_MAX) return hipErrorInvalidValue;
-  // the interior kernel's conditions: whole stages in K, 16-byte output rows,
-  // vector-aligned scales and bias; then every tile wholly inside M and N
-  // takes it, and the edge kernel the rest
-  // (configurations that stage their epilogue vectors in LDS also need K > 0
-  // and 16-byte aligned s_x and bias for the 16-byte direct-to-LDS loads)
+  // the interior kernel's conditions: whole stages in K and 16-byte output
+  // rows; then every tile wholly inside M and N takes it, and the edge
+  // kernel the rest.  Its vector form (VEC) also needs 16-byte aligned s_w
+  // and 8-byte aligned bias, and configurations that stage their epilogue
+  // vectors in LDS K > 0 and 16-byte aligned s_x and bias (16-byte
+  // direct-to-LDS loads); otherwise the interior tiles read the vectors
+  // element by element
   const bool epi = C::kEpiLds && !I32;
-  const bool interior = (a.N % 8 == 0) && (a.K % C::BK == 0) &&
-                        (reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
-                        (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0) &&
-                        (!epi || (a.K > 0 && reinterpret_cast<uintptr_t>(a.sx) % 16 == 0 &&
-                                  reinterpret_cast<uintptr_t>(a.bias) % 16 == 0));
+  const bool interior = (a.N % 8 == 0) && (a.K % C::BK == 0);
+  const bool vec = I32 || ((reinterpret_cast<uintptr_t>(a.sw) % 16 == 0) &&
+                           (reinterpret_cast<uintptr_t>(a.bias) % 8 == 0) &&
+                           (!epi || (a.K > 0 && reinterpret_cast<uintptr_t>(a.sx) % 16 == 0 &&
+                                     reinterpret_cast<uintptr_t>(a.bias) % 16 == 0)));
   const int64_t MTi = interior ? a.M / C::BM : 0;
   const int64_t NTi = interior ? a.N / C::BN : 0;
   const int64_t Ti = MTi * NTi;
   const int64_t E = interior ? (MT > MTi ? NT : 0) + (NT > NTi ? MTi : 0) : MT * NT;
   int grid = 0;
   if (Ti > 0) {
-    hipError_t e = persistent_grid<gemm_kernel<C, I32, false>>(C::kThreads, Ti, grid);
-    if (e != hipSuccess) return e;
-    gemm_kernel<C, I32, false><<<dim3(grid), dim3(C::kThreads), 0, stream>>>(
-        a, static_cast<int>(Ti), static_cast<int>(MT), static_cast<int>(NT), static_cast<int>(MTi),
-        static_cast<int>(NTi), 0);
-    e = hipGetLastError();
+    hipError_t e = vec ? launch_interior<C, I32, true>(a, Ti, MT, NT, MTi, NTi, stream)
+                       : launch_interior<C, I32, false>(a, Ti, MT, NT, MTi, NTi, stream);
     if (e != hipSuccess) return e;
   }
   if (E > 0) {
