@@ -130,6 +130,16 @@ def _counter_rows(folder, counter):
     return rows
 
 
+def up_kernel_name(cfg_name):
+    """The leading part of the up-proj GEMM kernel's name as the profiler
+    prints it, for its configuration: the ping-pong kernel (names ending in
+    _pp) or the tiled kernel, with the tile's size."""
+    import re
+    bm, bn = (int(v) for v in re.match(r"bm(\d+)_bn(\d+)_", cfg_name).groups())
+    kern = "gemm_pp_kernel" if cfg_name.endswith("_pp") else "gemm_kernel"
+    return f"{kern}<w8a8::(anonymous namespace)::Tile<{bm}, {bn},"
+
+
 def write_traffic(gf, gw, cf, cw):
     """Per-launch HBM bytes of the up-proj GEMM (the dispatch of the gemm kernel
     with the up-proj grid) from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
@@ -141,17 +151,13 @@ def write_traffic(gf, gw, cf, cw):
             raise SystemExit(f"no copy kernel rows for {counter} in {folder}")
         return max(vals) / COPY_BYTES  # counter bytes per real byte
 
-    import re
-
     import w8a8_int8_quantized_quantize_amd as w8
     name = w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(4096, 12288, 3072))
     down = w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(4096, 3072, 12288))
-    bm, bn = (int(v) for v in re.match(r"bm(\d+)_bn(\d+)_", name).groups())
-    tile = f"Tile<{bm}, {bn},"  # the up-proj kernel's template arguments
+    kname = up_kernel_name(name)
 
     def gemm_bytes(folder, counter):
-        rows = sorted((r for r in _counter_rows(folder, counter)
-                       if "gemm_kernel" in r["Kernel_Name"] and tile in r["Kernel_Name"]),
+        rows = sorted((r for r in _counter_rows(folder, counter) if kname in r["Kernel_Name"]),
                       key=lambda r: int(r["Dispatch_Id"]))
         if down == name:  # one kernel for both: the step launches up-proj first
             rows = rows[::2]
@@ -162,7 +168,7 @@ def write_traffic(gf, gw, cf, cw):
 
     ff, fw = copy_factor(cf, "FETCH_SIZE"), copy_factor(cw, "WRITE_SIZE")
     (fb, nf), (wb, nw) = gemm_bytes(gf, "FETCH_SIZE"), gemm_bytes(gw, "WRITE_SIZE")
-    out = {"kernel": f"gemm_kernel ({name}), up-proj M=4096 K=3072 N=12288",
+    out = {"kernel": f"{kname}...> ({name}), up-proj M=4096 K=3072 N=12288",
            "gemm_src_sha256_16": gemm_src_hash(),
            "fetch_bytes_per_launch": fb / ff, "write_bytes_per_launch": wb / fw,
            "bytes_per_launch": fb / ff + wb / fw,
@@ -625,6 +631,7 @@ def main():
     q_bytes = 3.0 * up.M * up.K + 4 * up.M
     g_bytes = 3.0 * down.M * down.K + 4 * down.M
 
+    up_cfg = w8.w8a8_gemm_config_name(w8.w8a8_gemm_select_config(up.M, up.N, up.K))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -644,8 +651,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gemm_up_tops, 1), "peak": PEAK_INT8_TOPS,
                      "unit": "TOP/s", "frac": round(gemm_up_tops / PEAK_INT8_TOPS, 4),
                      "traffic": traffic_entry(),
-                     "kernel": "gemm_kernel, up-proj M=4096 K=3072 N=12288 (int8 ops per launch "
-                               "2*M*N*K / mean HIP-event duration)"},
+                     "kernel": f"{up_kernel_name(up_cfg)}...> ({up_cfg}), up-proj M=4096 K=3072 "
+                               "N=12288 (int8 ops per launch 2*M*N*K / mean HIP-event duration)"},
         # the fused entry w8a8_linear at the headline shape (quantize + GEMM +
         # epilogue, one call), event-timed in every step of timed region 1
         "fused_linear": {"entry": "w8a8_linear", "M": up.M, "K": up.K, "N": up.N,
