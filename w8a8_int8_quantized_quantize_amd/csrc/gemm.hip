@@ -2038,10 +2038,10 @@ const MeasuredChoice kMeasured[] = {
     {16, 3072, 3072, 8},
     {256, 18432, 3072, 2},     // bm256_bn128_bk128_s3_mf32
     {256, 3072, 3072, 13},     // rows64_bn48_splitk8_mf16
-    {4608, 9216, 3072, 12},    // 1024px block chain, all four GEMMs: the ping-pong tile
-    {4608, 3072, 3072, 12},
-    {4608, 12288, 3072, 12},
-    {4608, 3072, 12288, 12},
+    {4608, 9216, 3072, 12},    // 1024px block chain: the ping-pong tile, except the
+    {4608, 3072, 3072, 12},    // down-projection, where the 8-wave generic tile was faster
+    {4608, 12288, 3072, 12},   // in three interleaved rounds of 100 calls (162-164 against
+    {4608, 3072, 12288, 11},   // 165-167 us)
 };
 const MeasuredChoice kFp8Measured[] = {
     {64, 128, 256, 3},         // fp8_few_rows_splitk4_mf16
