@@ -527,7 +527,8 @@ __device__ __forceinline__ uint4 gelu8(uint4 o) {
 // Interior-tile bf16 epilogue, stored straight from the MFMA layout.  All
 // scales and biases the lane needs are fetched up front (four consecutive
 // columns at a time), then each accumulator block is dequantized and
-// written as 8-byte runs.
+// written in 16-byte runs (8-byte runs for 16x16 blocks without a partner
+// row block).
 // EPI: the tile's scales and bias were staged in LDS (stage_epilogue_vectors)
 // and are read from there; otherwise from global memory, with 16-byte s_w
 // and 8-byte bias loads when VEC (the vectors are aligned for them), else
@@ -1396,14 +1397,15 @@ __global__ __launch_bounds__(C::kThreads) void gemm_pp_kernel(GemmArgs a, int T,
 // registers (ST 64-byte K steps in flight per wave, no LDS staging),
 // accumulating with v_mfma_i32_16x16x64_i8, then the waves' partial sums
 // meet in LDS and the MB x NB result blocks are shared out over the waves
-// for the reduction and the epilogue.  The int8 configurations load
-// coalesced (COAL, below) and permute into the MFMA layout: a load in that
-// layout puts four different rows under every four consecutive lanes, and
-// it measured 5-9% slower on the weight-streaming shapes (1 and 16 rows)
-// and 1.8x slower at 256 rows than the coalesced load plus the permute.  grid.y covers M in steps of 16 MB, so
-// any M works.  MB = 1 is the few-row kernel proper; MB = 4 (64 rows) serves
-// a few hundred tokens, where the tiled kernel's large tiles would leave
-// most CUs idle: 64 x 48 blocks make 256 workgroups of a 256 x 3072 output.
+// for the reduction and the epilogue.  grid.y covers M in steps of 16 x MB
+// rows, so any M works.  MB = 1 is the few-row kernel proper; MB = 4 (64
+// rows) serves a few hundred tokens, where the tiled kernel's large tiles
+// would leave most CUs idle: 64 x 48 blocks make 256 workgroups of a
+// 256 x 3072 output.  The int8 configurations load coalesced (COAL, below)
+// and permute into the MFMA layout: loaded in that layout, every four
+// consecutive lanes read four different rows, which measured 5-9% slower on
+// the weight-streaming shapes (1 and 16 rows) and 1.8x slower at 256 rows
+// than the coalesced load plus the permute.
 //   MFMA 16x16x64 layout: lane l holds row l % 16 of a 16-row operand, K
 //   bytes 16 (l / 16) .. +15 of a 64-byte step; D[i][j] (i: weight row n,
 //   j: token m) sits in lane j + 16 (i / 4), register i % 4.
@@ -1443,9 +1445,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * 16 * MB;
   const int r = lane % 16, kq = lane / 16;
   // COAL: each lane loads row lane / 4, piece lane % 4 (four consecutive lanes
-  // read one 64-byte run of a row, so a load instruction touches 16 cache
-  // lines rather than 64), and a ds_bpermute then moves every fragment into
-  // the MFMA layout above (lane d takes lane 4 (d % 16) + d / 16's piece)
+  // read one 64-byte run of a row; the instruction reads the same 16 rows x
+  // 64 bytes as in the MFMA layout), and a ds_bpermute then moves every
+  // fragment into the MFMA layout above (lane d takes lane 4 (d % 16) +
+  // d / 16's piece)
   const int lr = COAL ? lane / 4 : r, lq = COAL ? lane % 4 : kq;
   const int perm = 4 * (4 * (lane % 16) + lane / 16);  // bpermute byte address
   const int64_t steps = (K + SB - 1) / SB;
