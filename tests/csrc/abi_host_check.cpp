@@ -51,11 +51,11 @@ hipError_t noalloc_scratch(void** ptr) {
   *ptr = g_scratch_stub;  // stands in for the device scratch
   return hipSuccess;
 }
-int g_rows = 0;
-bool linear_few_rows_supported(int64_t M, int64_t, int64_t K) { return M <= 2 && K <= 3072; }
-hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t) {
+int g_rows = 0, g_rows_fp8 = 0;
+bool linear_few_rows_supported(int64_t M, int64_t, int64_t K, bool) { return M <= 2 && K <= 3072; }
+hipError_t launch_linear_few_rows(const RowsArgs& a, bool fp8, hipStream_t) {
   CHECK(a.M >= 1 && a.M <= 2 && a.qx_out != nullptr && a.sx_out != nullptr && a.y != nullptr);
-  ++g_rows;
+  ++(fp8 ? g_rows_fp8 : g_rows);
   return hipSuccess;
 }
 int g_gelu_gemm = 0, g_quant_amax = 0;
@@ -201,6 +201,10 @@ int main() {
   CHECK(w8a8_linear_fp8(x.data(), w8, sw.data(), nullptr, M, N, K, y.data(), ws_buf, 16, nullptr) ==
         W8A8_ERR_WORKSPACE);
   CHECK(g_gemm_fp8 == 2 && g_quant == 9);
+  // a handful of tokens: the single-launch fused kernel with e4m3 codes
+  CHECK(w8a8_linear_fp8(x.data(), w8, sw.data(), nullptr, 2, N, K, y.data(), ws_buf, need, nullptr) ==
+        W8A8_OK);
+  CHECK(w8a8::g_rows_fp8 == 1 && w8a8::g_rows == 1 && g_gemm_fp8 == 2 && g_quant == 9);
 
   // GELU-epilogue GEMM and the absmax-given quantizer (the inter-layer fusion variant)
   {

@@ -245,3 +245,37 @@ def test_fp8_accumulation_error_calibration(K):
           f"in units of sum|ab|: " + ", ".join(f"{k} 2^{np.log2(max(v, 2.0 ** -60)):.2f}"
                                             for k, v in worst.items()))
 
+
+
+# The single-launch FP8 linear for up to 4 token rows (e4m3 quantization, GEMM
+# and epilogue in one kernel): the same codes and scales in the workspace as
+# the e4m3 quantizer writes, and the same output bits as the two launches
+# (quantizer + the FP8 few-row GEMM) it replaces.  K tails that are not a
+# multiple of the 128-byte step, N not a multiple of 16, an all-zero row and
+# a subnormal-range row; (9, 272, 2000) takes the two-launch path.
+@pytest.mark.parametrize("M,N,K", [(1, 3072, 3072), (4, 3072, 3072), (3, 100, 1040), (3, 16, 16),
+                                   (1, 18432, 3072), (2, 40, 48), (4, 272, 2000), (1, 16, 3072),
+                                   (9, 272, 2000)])
+def test_linear_fp8_few_rows_single_launch(M, N, K):
+    rng = np.random.default_rng(M * 1000 + K + N)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    if M >= 3:
+        xb[1] = 0                                    # all-zero row
+        xb[2] = rand_bits(rng, 1, K, scale=1e-39)[0]  # subnormal-range row
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0]
+    wq, sw = w8.w8a8_quantize_weight_fp8(torch.from_numpy(w).to(DEV))
+    qx, sx = oracle.quantize_rows_bf16_fp8(xb)
+    qw, swo = oracle.quantize_rows_f32_fp8(w)
+    x = dev_bf16(xb)
+    q2, s2 = w8.w8a8_quantize_act_fp8(x)
+    assert np.array_equal(host(q2), qx) and np.array_equal(host(s2).view(np.uint32), sx.view(np.uint32))
+    ws = torch.full((w8.w8a8_linear_workspace_bytes(M, K),), 0x55, dtype=torch.uint8, device=DEV)
+    pad = (M * K + 255) // 256 * 256
+    for bias, b_bits in ((dev_bf16(bb), bb), (None, None)):
+        y = w8.w8a8_linear_fp8(x, wq, sw, bias, workspace=ws)
+        assert np.array_equal(host(ws[:M * K]).reshape(M, K), qx)
+        assert np.array_equal(host(ws[pad:pad + 4 * M]).view(np.uint32), sx.view(np.uint32))
+        y2 = w8.w8a8_gemm_dequant_fp8(q2, s2, wq, sw, bias)
+        assert torch.equal(y, y2)
+        assert_fp8_gemm_bound(bits(y), qx, sx, qw, swo, b_bits, f"linear_fp8 {M}x{N}x{K}")

@@ -203,7 +203,7 @@ int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w, const v
   if (int rc = check_rows(x_bf16, M, K, K, 2, qx, K, sx)) return rc;
   if (int rc = check_gemm(qx, w_q, M, N, K, y_bf16)) return rc;
   if (int rc = check_dequant(sx, s_w, bias_bf16, M, N)) return rc;
-  if (w8a8::linear_few_rows_supported(M, N, K)) {
+  if (w8a8::linear_few_rows_supported(M, N, K, false)) {
     // a handful of tokens: quantize, GEMM and epilogue in one launch, which
     // also leaves the codes and scales in the workspace
     w8a8::RowsArgs r;
@@ -217,7 +217,7 @@ int w8a8_linear(const void* x_bf16, const int8_t* w_q, const float* s_w, const v
     r.M = M;
     r.N = N;
     r.K = K;
-    return hip_status(w8a8::launch_linear_few_rows(r, as_stream(stream)));
+    return hip_status(w8a8::launch_linear_few_rows(r, false, as_stream(stream)));
   }
   if (int rc = hip_status(w8a8::launch_quantize_rows(QuantSrc::kBf16, x_bf16, M, K, K, qx, K, sx,
                                                      nullptr, as_stream(stream))))
@@ -335,6 +335,22 @@ int w8a8_linear_fp8(const void* x_bf16, const uint8_t* w_q, const float* s_w,
   if (int rc = check_rows(x_bf16, M, K, K, 2, qx, K, sx)) return rc;
   if (int rc = check_gemm(qx, reinterpret_cast<const int8_t*>(w_q), M, N, K, y_bf16)) return rc;
   if (int rc = check_dequant(sx, s_w, bias_bf16, M, N)) return rc;
+  if (w8a8::linear_few_rows_supported(M, N, K, true)) {
+    // a handful of tokens: the e4m3 quantization, GEMM and epilogue in one
+    // launch (the same bits as the two launches below)
+    w8a8::RowsArgs r;
+    r.x = static_cast<const uint16_t*>(x_bf16);
+    r.qw = reinterpret_cast<const int8_t*>(w_q);
+    r.sw = s_w;
+    r.bias = static_cast<const uint16_t*>(bias_bf16);
+    r.y = static_cast<uint16_t*>(y_bf16);
+    r.qx_out = qx;
+    r.sx_out = sx;
+    r.M = M;
+    r.N = N;
+    r.K = K;
+    return hip_status(w8a8::launch_linear_few_rows(r, true, as_stream(stream)));
+  }
   if (int rc = hip_status(w8a8::launch_quantize_rows(QuantSrc::kBf16Fp8, x_bf16, M, K, K, qx, K,
                                                      sx, nullptr, as_stream(stream))))
     return rc;

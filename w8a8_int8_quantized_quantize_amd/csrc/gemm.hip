@@ -1629,11 +1629,21 @@ constexpr int kRowsMaxK = 3072;  // codes of 16 rows of up to this K fit the LDS
 // the single launch is taken for up to 4 rows (measured slower than the two
 // launches at 16 rows, where each workgroup quantizes 49152 elements).
 constexpr int kRowsMaxM = 4;
-template <int CH, int ST>
+// FP8: the same with e4m3 codes (scale absmax / 448) and
+// v_mfma_scale_f32_16x16x128_f8f6f4: 128-byte K steps, a lane's operand is 32
+// bytes of its row (two 16-byte pieces), fp32 partial sums added in wave
+// order; the weights are loaded in the MFMA layout and the pieces past K
+// zeroed exactly as the FP8 few-row GEMM does, so the output is the same
+// bits as the two-launch path (e4m3 quantizer + FP8 few-row GEMM).
+template <int CH, int ST, bool FP8 = false>
 __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
   constexpr int NW = 4;
+  constexpr int SB = FP8 ? 128 : 64;  // K bytes of one MFMA
+  constexpr int PB = SB / 4;          // K bytes of one lane's operand
+  using Frag = std::conditional_t<FP8, v8i, v4i>;
+  using Acc = std::conditional_t<FP8, v4f, v4i>;
   __shared__ __attribute__((aligned(16))) int8_t codes[16 * (kRowsMaxK + 16)];
-  __shared__ v4i part[NW][64];
+  __shared__ Acc part[NW][64];
   __shared__ uint32_t amax_bits[16];
   __shared__ float srow[16];
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -1643,7 +1653,7 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
   const int64_t ldc = K + 16;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int r = lane % 16, kq = lane / 16;
-  const int64_t steps = (K + 63) / 64;
+  const int64_t steps = (K + SB - 1) / SB;
   const int64_t per = (steps + NW - 1) / NW;
   const int64_t s0 = wave * per, s1 = min(steps, s0 + per);
   if (t < 16) amax_bits[t] = 0u;
@@ -1674,17 +1684,26 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
   // the weight fragments of this wave's K share (past the share or past K:
-  // clamped to offset 0, never used), loaded four lanes to a 64-byte run of
-  // a row (lane l: row l / 4, piece l % 4) and moved into the MFMA layout by
-  // a ds_bpermute before use (lane d takes lane 4 (d % 16) + d / 16's piece)
-  const int8_t* wrow = a.qw + min(n0 + lane / 4, N - 1) * K;
+  // clamped into the row, never used).  int8: loaded four lanes to a 64-byte
+  // run of a row (lane l: row l / 4, piece l % 4) and moved into the MFMA
+  // layout by a ds_bpermute before use (lane d takes lane 4 (d % 16) + d /
+  // 16's piece).  FP8: loaded in the MFMA layout, two 16-byte pieces.
+  const int8_t* wrow = a.qw + min(n0 + (FP8 ? r : lane / 4), N - 1) * K;
   const int perm = 4 * (4 * (lane % 16) + lane / 16);
-  v4i wf[ST];
+  Frag wf[ST];
 #pragma unroll
   for (int i = 0; i < ST; ++i) {
-    const int64_t k = (s0 + i) * 64 + (lane % 4) * 16;
-    const int64_t kc = ((s0 + i) < s1 && k < K) ? k : 0;
-    wf[i] = *reinterpret_cast<const v4i*>(wrow + kc);
+    const int64_t k = (s0 + i) * SB + (FP8 ? kq : lane % 4) * PB;
+    const bool in = (s0 + i) < s1 && k < K;
+    const int64_t kc = in ? k : 0;
+    if constexpr (FP8) {
+      const int64_t kc2 = (in && k + 16 < K) ? k + 16 : kc;
+      const v4i lo = *reinterpret_cast<const v4i*>(wrow + kc);
+      const v4i hi = *reinterpret_cast<const v4i*>(wrow + kc2);
+      wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      wf[i] = *reinterpret_cast<const v4i*>(wrow + kc);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();  // amax_bits cleared
@@ -1709,7 +1728,7 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
     }
   }
   __syncthreads();
-  if (t < 16 && t < M) srow[t] = __uint_as_float(amax_bits[t]) / 127.0f;
+  if (t < 16 && t < M) srow[t] = __uint_as_float(amax_bits[t]) / kCodeMax<FP8>;
   __syncthreads();
   // codes into the LDS copy
   int row = row0, pos = pos0;
@@ -1719,16 +1738,9 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
       const float s = srow[row];
       uint2 p = make_uint2(0u, 0u);
       if (s >= kFastMinScale) {
-        const float rcp = 1.0f / s;
-        p.x = pack4(code_word<2>(bf_lo(xv[j].x), s, rcp), code_word<2>(bf_hi(xv[j].x), s, rcp),
-                    code_word<2>(bf_lo(xv[j].y), s, rcp), code_word<2>(bf_hi(xv[j].y), s, rcp));
-        p.y = pack4(code_word<2>(bf_lo(xv[j].z), s, rcp), code_word<2>(bf_hi(xv[j].z), s, rcp),
-                    code_word<2>(bf_lo(xv[j].w), s, rcp), code_word<2>(bf_hi(xv[j].w), s, rcp));
+        p = codes_bf16x8<2, FP8>(xv[j], s, 1.0f / s);
       } else if (s != 0.0f) {
-        p.x = pack4(code_word<1>(bf_lo(xv[j].x), s, 0.f), code_word<1>(bf_hi(xv[j].x), s, 0.f),
-                    code_word<1>(bf_lo(xv[j].y), s, 0.f), code_word<1>(bf_hi(xv[j].y), s, 0.f));
-        p.y = pack4(code_word<1>(bf_lo(xv[j].z), s, 0.f), code_word<1>(bf_hi(xv[j].z), s, 0.f),
-                    code_word<1>(bf_lo(xv[j].w), s, 0.f), code_word<1>(bf_hi(xv[j].w), s, 0.f));
+        p = codes_bf16x8<1, FP8>(xv[j], s, 0.0f);
       }
       *reinterpret_cast<uint2*>(codes + row * ldc + pos * 8) = p;
       if (blockIdx.x == 0 && a.qx_out != nullptr)
@@ -1745,19 +1757,28 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
   __syncthreads();
   // MFMAs over the wave's K share; rows past M read row M - 1 of the copy
   const int8_t* crow_l = codes + min<int64_t>(r, M - 1) * ldc;
-  v4i acc = {0, 0, 0, 0};
+  Acc acc = {};
 #pragma unroll
   for (int i = 0; i < ST; ++i) {
     if (s0 + i >= s1) break;  // wave-uniform
-    const int64_t k = (s0 + i) * 64 + kq * 16;
-    v4i xq = {0, 0, 0, 0};
-    if (k < K) xq = *reinterpret_cast<const v4i*>(crow_l + k);
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(to_mfma_layout(wf[i], perm), xq, acc, 0, 0, 0);
+    const int64_t k = (s0 + i) * SB + kq * PB;
+    if constexpr (FP8) {
+      // pieces past K are zero (the copy's row padding is never used)
+      v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
+      if (k < K) lo = *reinterpret_cast<const v4i*>(crow_l + k);
+      if (k + 16 < K) hi = *reinterpret_cast<const v4i*>(crow_l + k + 16);
+      const v8i xq = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], xq, acc, 0, 0, 0, 127, 0, 127);
+    } else {
+      v4i xq = {0, 0, 0, 0};
+      if (k < K) xq = *reinterpret_cast<const v4i*>(crow_l + k);
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(to_mfma_layout(wf[i], perm), xq, acc, 0, 0, 0);
+    }
   }
   part[wave][lane] = acc;
   __syncthreads();
   if (wave != 0 || r >= M) return;
-  v4i tt = part[0][lane];
+  Acc tt = part[0][lane];
 #pragma unroll
   for (int w = 1; w < NW; ++w) tt += part[w][lane];
   const float s = srow[r];
@@ -1807,22 +1828,22 @@ hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
   return launch_few_rows_st<NW, NB, I32, STLOOP, true, FP8, MB, COAL>(a, stream);
 }
 
-template <int CH, int ST>
+template <int CH, int ST, bool FP8>
 hipError_t launch_linear_few_rows_st(const RowsArgs& a, hipStream_t stream) {
   const int64_t gx = (a.N + 15) / 16;
   if (gx > INT32_MAX) return hipErrorInvalidValue;
-  linear_few_rows<CH, ST><<<dim3(static_cast<unsigned>(gx)), dim3(256), 0, stream>>>(a);
+  linear_few_rows<CH, ST, FP8><<<dim3(static_cast<unsigned>(gx)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 // Chunks of x per thread: CH covering M x K / 8 over 256 threads.
-template <int ST>
+template <int ST, bool FP8>
 hipError_t launch_linear_few_rows_ch(const RowsArgs& a, hipStream_t stream) {
   const int64_t ch = (a.M * (a.K / 8) + 255) / 256;
-  if (ch <= 1) return launch_linear_few_rows_st<1, ST>(a, stream);
-  if (ch <= 2) return launch_linear_few_rows_st<2, ST>(a, stream);
-  if (ch <= 4) return launch_linear_few_rows_st<4, ST>(a, stream);
-  if (ch <= 6) return launch_linear_few_rows_st<6, ST>(a, stream);
+  if (ch <= 1) return launch_linear_few_rows_st<1, ST, FP8>(a, stream);
+  if (ch <= 2) return launch_linear_few_rows_st<2, ST, FP8>(a, stream);
+  if (ch <= 4) return launch_linear_few_rows_st<4, ST, FP8>(a, stream);
+  if (ch <= 6) return launch_linear_few_rows_st<6, ST, FP8>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -2196,23 +2217,34 @@ hipError_t launch_gemm_gelu_amax(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The single-launch fused linear takes M <= 16 rows whose K fits one chunk
-// of at most 12 64-element steps per wave (K <= 3072 with 4 waves), where the
-// library would run the few-row GEMM.
-bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K) {
+// The single-launch fused linear takes up to kRowsMaxM rows whose codes fit
+// the LDS copy (K <= 3072: at most 12 64-byte or 6 128-byte steps per wave),
+// where the library would run the few-row GEMM.
+bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K, bool fp8) {
   if (M < 1 || M > kRowsMaxM || N < 1 || K < 16 || K % 16 != 0 || K > kRowsMaxK) return false;
-  return gemm_select_config(M, N, K) == kFewRows;
+  return fp8 ? gemm_fp8_select_config(M, N, K) == kFp8FewRows
+             : gemm_select_config(M, N, K) == kFewRows;
 }
 
-hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t stream) {
+hipError_t launch_linear_few_rows(const RowsArgs& a, bool fp8, hipStream_t stream) {
+  if (fp8) {
+    const int64_t per = ((a.K + 127) / 128 + 3) / 4;  // 128-byte steps per wave
+    switch (per) {
+      case 1: return launch_linear_few_rows_ch<1, true>(a, stream);
+      case 2: return launch_linear_few_rows_ch<2, true>(a, stream);
+      case 3: case 4: return launch_linear_few_rows_ch<4, true>(a, stream);
+      case 5: case 6: return launch_linear_few_rows_ch<6, true>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const int64_t per = ((a.K + 63) / 64 + 3) / 4;  // 64-byte steps per wave
   switch (per) {
-    case 1: return launch_linear_few_rows_ch<1>(a, stream);
-    case 2: return launch_linear_few_rows_ch<2>(a, stream);
-    case 3: case 4: return launch_linear_few_rows_ch<4>(a, stream);
-    case 5: case 6: return launch_linear_few_rows_ch<6>(a, stream);
-    case 7: case 8: return launch_linear_few_rows_ch<8>(a, stream);
-    case 9: case 10: case 11: case 12: return launch_linear_few_rows_ch<12>(a, stream);
+    case 1: return launch_linear_few_rows_ch<1, false>(a, stream);
+    case 2: return launch_linear_few_rows_ch<2, false>(a, stream);
+    case 3: case 4: return launch_linear_few_rows_ch<4, false>(a, stream);
+    case 5: case 6: return launch_linear_few_rows_ch<6, false>(a, stream);
+    case 7: case 8: return launch_linear_few_rows_ch<8, false>(a, stream);
+    case 9: case 10: case 11: case 12: return launch_linear_few_rows_ch<12, false>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -45,8 +45,9 @@ struct RowsArgs {
   float* sx_out;         // [M] scales of x, or nullptr
   int64_t M, N, K;
 };
-bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K);
-hipError_t launch_linear_few_rows(const RowsArgs& a, hipStream_t stream);
+// (fp8: e4m3 codes of x and weights, the FP8 GEMM's few-row kernel's bits)
+bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K, bool fp8);
+hipError_t launch_linear_few_rows(const RowsArgs& a, bool fp8, hipStream_t stream);
 
 // The GEMM whose epilogue also applies GELU and raises the row maxima of |h|
 // (the inter-layer fusion variant): out = h = bf16(gelu(y)) [M, N] bf16,

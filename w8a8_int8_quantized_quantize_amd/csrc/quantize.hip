@@ -100,58 +100,6 @@ __device__ __forceinline__ void load_row(const uint4* src, uint32_t nch, uint32_
   }
 }
 
-// FP8 (OCP e4m3) codes of four quotients: each clamped to the largest finite
-// e4m3 magnitude, 448 (so that a quotient inflated by a coarse subnormal
-// scale cannot become NaN), then converted two at a time with
-// v_cvt_pk_fp8_f32, which rounds to the nearest e4m3 value, ties to even.
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
-}
-
-// Largest code magnitude: the row's absmax maps to it.
-template <bool FP8>
-constexpr float kCodeMax = FP8 ? 448.0f : 127.0f;
-
-// The quotient x / s of the codes: MODE 1 the IEEE division, MODE 2 the
-// reciprocal with one Markstein correction.  For scales absmax / 448 the
-// latter differs from the division in the last bit on about 0.2% of bf16
-// pairs, yet never in the e4m3 code it rounds to (checked over every pair of
-// bf16 values with scale >= 2^-96 on the CPU).  The correction turns x = -0
-// into +0 (-0 + +0 rounds to +0); s > 0, so the quotient takes the sign of x,
-// which keeps e4m3's signed zero (code 0x80) as the division would.
-template <int MODE>
-__device__ __forceinline__ float quotient(float x, float s, float r) {
-  if constexpr (MODE == 1) {
-    return x / s;
-  } else {
-    const float q = x * r;
-    return __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q, s, x), r, q), x);
-  }
-}
-
-// Eight codes of a 16-byte chunk of bf16 values.
-template <int MODE, bool FP8 = false>
-__device__ __forceinline__ uint2 codes_bf16x8(const uint4 raw, float s, float r) {
-  uint2 p;
-  if constexpr (FP8) {
-    p.x = fp8x4(quotient<MODE>(bf_lo(raw.x), s, r), quotient<MODE>(bf_hi(raw.x), s, r),
-                quotient<MODE>(bf_lo(raw.y), s, r), quotient<MODE>(bf_hi(raw.y), s, r));
-    p.y = fp8x4(quotient<MODE>(bf_lo(raw.z), s, r), quotient<MODE>(bf_hi(raw.z), s, r),
-                quotient<MODE>(bf_lo(raw.w), s, r), quotient<MODE>(bf_hi(raw.w), s, r));
-  } else {
-    p.x = pack4(code_word<MODE>(bf_lo(raw.x), s, r), code_word<MODE>(bf_hi(raw.x), s, r),
-                code_word<MODE>(bf_lo(raw.y), s, r), code_word<MODE>(bf_hi(raw.y), s, r));
-    p.y = pack4(code_word<MODE>(bf_lo(raw.z), s, r), code_word<MODE>(bf_hi(raw.z), s, r),
-                code_word<MODE>(bf_lo(raw.w), s, r), code_word<MODE>(bf_hi(raw.w), s, r));
-  }
-  return p;
-}
-
 template <bool FP8 = false>
 __device__ __forceinline__ uint32_t codes_f32x4(const uint4 raw, float s) {
   if (s == 0.0f) return 0u;
