@@ -131,6 +131,8 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
  *   workspace  device memory of at least w8a8_linear_workspace_bytes(M, K),
  *              16-byte aligned; its contents on return are the codes and
  *              scales of x.  Calls sharing one workspace must be ordered.
+ * For a few token rows (M <= 8, or M <= 12 with N <= 4096; K <= 3072) the
+ * quantization, the GEMM and the epilogue run in one kernel launch.
  * Source: the Abstract's fused INT8 GEMM that replaces the
  * dequantize-to-bf16 linear forward.
  */
@@ -267,7 +269,8 @@ const char* w8a8_gemm_fp8_config_name(int config);
 /*
  * The fused FP8 linear: w8a8_quantize_act_fp8 of x into the workspace (same
  * size as w8a8_linear's: w8a8_linear_workspace_bytes(M, K)), then
- * w8a8_gemm_dequant_fp8.  w_q, s_w from w8a8_quantize_weight_fp8.
+ * w8a8_gemm_dequant_fp8.  w_q, s_w from w8a8_quantize_weight_fp8.  The same
+ * few-row cases as w8a8_linear run in one launch (same output bits).
  */
 int w8a8_linear_fp8(const void* x_bf16, const uint8_t* w_q, const float* s_w,
                     const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,

@@ -1609,26 +1609,30 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
 // The whole fused linear for M <= 16 token rows in one launch.  Each
 // workgroup owns 16 output columns; its 4 waves split K for the MFMAs as in
 // gemm_few_rows.  Before them, the workgroup quantizes the M x K activations
-// itself: its 256 threads take the 16-byte chunks of x [M, K] in turn, reduce
-// each row's absmax in LDS (an atomic max on the magnitude's bit pattern,
-// exact in any order), and write the codes, computed with the row
-// quantizer's own operations (quant_codes.h, the same bits
-// w8a8_quantize_act writes), into an LDS copy of the codes; each lane then
-// reads its MFMA operand from there.  The activations are loaded before the
-// weight fragments (loads complete in issue order), so they are quantized
-// while the weights stream in.  Every workgroup reads all of x (at most
-// 16 x 3072 bf16, L2-resident after the first), in place of a separate
-// quantize launch and the gap before the GEMM's.  Column block 0 also writes
-// the codes and scales to the workspace, as the two-launch path does.
-//   Operand layout (below): lane l holds token row l % 16 and K bytes
-//   32 (l / 16) .. +31 of a 128-byte step: two 16-byte LDS reads.
+// itself, one wave per row as the row quantizer does (wave w takes rows w,
+// w + 4, ...): each lane loads 16-byte chunks lane, lane + 64, ... of the
+// row, the wave reduces the row's absmax with cross-lane maxima, and the
+// codes, computed with the row quantizer's own operations (quant_codes.h,
+// the same bits w8a8_quantize_act writes), go into an LDS copy of the codes;
+// each lane then reads its MFMA operand from there.  The activations are
+// loaded before the weight fragments (loads complete in issue order), so
+// they are quantized while the weights stream in.  Every workgroup reads all
+// of x (at most 16 x 3072 bf16, L2-resident after the first), in place of a
+// separate quantize launch and the gap before the GEMM's.  Column block 0
+// also writes the codes and scales to the workspace, as the two-launch path
+// does.
 // LDS copy of the codes: row stride K + 16 bytes, so that the 16 rows of a
 // fragment read fall in 16 different 16-byte bank groups.
 constexpr int kRowsMaxK = 3072;  // codes of 16 rows of up to this K fit the LDS copy
-// Every workgroup quantizes all M rows, so the redundant work grows with M:
-// the single launch is taken for up to 4 rows (measured slower than the two
-// launches at 16 rows, where each workgroup quantizes 49152 elements).
-constexpr int kRowsMaxM = 4;
+// Every workgroup quantizes all M rows, so the redundant work grows with M
+// and with the number of column blocks: the single launch is taken for up to
+// 8 rows, and up to 12 while there are no more column blocks than CUs
+// (measured against the two launches at K = 3072: M = 4, N = 3072 9.2 ->
+// 7.8 us, N = 18432 20.2 -> 16.9 us; M = 8 11.2 -> 9.3 and 20.8 -> 20.2 us;
+// M = 12, N = 3072 11.8 -> 11.0 us, but N = 18432 23.0 -> 23.4 us, and
+// M = 16 no faster at either N).
+constexpr int kRowsMaxM = 12;
+constexpr int kRowsMaxMWide = 8;  // above kNumCU column blocks
 // K runs in 128-byte steps; lane l holds 32 bytes of row l % 16, K bytes
 // 32 (l / 16) .. +31 of a step (two 16-byte loads straight from the row).
 // int8: each step is two v_mfma_i32_16x16x64_i8, one on every lane's first
@@ -1640,19 +1644,24 @@ constexpr int kRowsMaxM = 4;
 // wave order; the weights are loaded and the pieces past K zeroed exactly as
 // the FP8 few-row GEMM does, so the output is the same bits as the two-launch
 // path (e4m3 quantizer + FP8 few-row GEMM).
-template <int CH, int ST, bool FP8 = false>
+// Rows over waves: WPR waves share a row when M < 4 (WPR = 4 / M, each wave
+// a 64-lane slice of every 64 WPR chunks, maxima joined in LDS); otherwise
+// wave w takes rows w, w + 4, ... (RPW of them).  A row has at most 64 ST
+// chunks (ST: the 128-byte steps of a wave's K share, 512 ST >= K).
+template <int WPR, int RPW, int ST, bool FP8 = false>
 __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
+  static_assert(WPR == 1 || RPW == 1, "shared rows: one per wave group");
   constexpr int NW = 4;
   constexpr int SB = 128;  // K bytes of one step
   constexpr int PB = 32;   // K bytes of one lane's operand in a step
+  constexpr int CHR = (ST + WPR - 1) / WPR;  // chunks of a row per lane
   using Acc = std::conditional_t<FP8, v4f, v4i>;
   __shared__ __attribute__((aligned(16))) int8_t codes[16 * (kRowsMaxK + 16)];
   __shared__ Acc part[NW][64];
-  __shared__ uint32_t amax_bits[16];
   __shared__ float srow[16];
+  __shared__ float wmax[NW];
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
-  const int t = threadIdx.x;
   const int64_t M = a.M, N = a.N, K = a.K;
   const int64_t ldc = K + 16;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
@@ -1660,7 +1669,6 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
   const int64_t steps = (K + SB - 1) / SB;
   const int64_t per = (steps + NW - 1) / NW;
   const int64_t s0 = wave * per, s1 = min(steps, s0 + per);
-  if (t < 16) amax_bits[t] = 0u;
   // epilogue scales and bias (clamped columns past N)
   float swe[4];
   uint32_t braw[4];
@@ -1673,19 +1681,25 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
       braw[e] = bsrc[n];
     }
   }
-  // this thread's chunks of x: flat chunk index c = t + 256 j over [M, K / 8];
-  // its row and position follow incrementally (no division per chunk)
-  const int ck = static_cast<int>(K / 8);  // chunks per row (K <= kRowsMaxK)
-  const int total = static_cast<int>(M) * ck;
-  const int q256 = 256 / ck, r256 = 256 % ck;
-  const int row0 = t / ck, pos0 = t % ck;
-  uint4 xv[CH];
+  // this wave's rows (row g + (NW / WPR) i, where it exists): chunks
+  // li + 64 WPR j of each (li: the lane's place in its row's WPR waves),
+  // clamped past the row's end to its last chunk (a copy of real elements,
+  // which leaves the absmax unchanged; its codes are not stored)
+  const int ck = static_cast<int>(K / 8);  // chunks per row, <= 64 ST
+  const int g = wave / WPR;
+  const int li = (wave % WPR) * 64 + lane;
+  uint4 xv[RPW][CHR];
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    const int c = t + 256 * j;
-    const int cc = c < total ? c : total - 1;  // clamped: a copy of a real chunk
-    xv[j] = reinterpret_cast<const uint4*>(a.x)[cc];
-    __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < RPW; ++i) {
+    const int row = g + (NW / WPR) * i;
+    if (row >= M) break;  // wave-uniform
+    const uint4* src = reinterpret_cast<const uint4*>(a.x) + static_cast<int64_t>(row) * ck;
+#pragma unroll
+    for (int j = 0; j < CHR; ++j) {
+      const int c = li + 64 * WPR * j;
+      xv[i][j] = src[c < ck ? c : ck - 1];
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // the weight pieces of this wave's K share (past the share or past K:
   // clamped into the row, and met by zeroed activation pieces)
@@ -1702,54 +1716,51 @@ __global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
     wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();  // amax_bits cleared
-  // row absmax: the magnitude bits of the largest element (non-negative
-  // values order as their bit patterns).  Chunk t + 256 j lies in row
-  // (row, pos), followed incrementally from (row0, pos0).
-  {
-    int row = row0, pos = pos0;
+  // per row: absmax (the magnitude bits of the largest element: non-negative
+  // values order as their bit patterns), scale, codes into the LDS copy
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      if (t + 256 * j < total) {
-        u16x2 m2 = {0, 0};
-        m2 = absmax2(absmax2(absmax2(absmax2(m2, xv[j].x), xv[j].y), xv[j].z), xv[j].w);
-        atomicMax(&amax_bits[row], __float_as_uint(absmax_of(m2)));
-      }
-      row += q256;
-      pos += r256;
-      if (pos >= ck) {
-        pos -= ck;
-        ++row;
+  for (int i = 0; i < RPW; ++i) {
+    const int row = g + (NW / WPR) * i;
+    float amax = 0.0f;
+    if (row < M) {  // wave-uniform
+      u16x2 m2 = {0, 0};
+#pragma unroll
+      for (int j = 0; j < CHR; ++j)
+        m2 = absmax2(absmax2(absmax2(absmax2(m2, xv[i][j].x), xv[i][j].y), xv[i][j].z), xv[i][j].w);
+      amax = wave_max(absmax_of(m2));
+    }
+    if constexpr (WPR > 1) {
+      // the row's maxima from its WPR waves (every wave passes the barrier)
+      if (lane == 0) wmax[wave] = amax;
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < WPR; ++v) amax = fmaxf(amax, wmax[g * WPR + v]);
+    }
+    if (row >= M) break;  // wave-uniform
+    const float s = amax / kCodeMax<FP8>;
+    if (lane == 0 && wave % WPR == 0) {
+      srow[row] = s;
+      if (blockIdx.x == 0 && a.sx_out != nullptr) a.sx_out[row] = s;
+    }
+    const int mode = s >= kFastMinScale ? 2 : (s != 0.0f ? 1 : 0);
+    const float rs = mode == 2 ? 1.0f / s : 0.0f;
+    int8_t* crow = codes + row * ldc;
+    int8_t* qrow = a.qx_out + static_cast<int64_t>(row) * K;
+    const bool out_codes = blockIdx.x == 0 && a.qx_out != nullptr;
+#pragma unroll
+    for (int j = 0; j < CHR; ++j) {
+      const int c = li + 64 * WPR * j;
+      if (c < ck) {
+        uint2 p = make_uint2(0u, 0u);
+        if (mode == 2)
+          p = codes_bf16x8<2, FP8>(xv[i][j], s, rs);
+        else if (mode == 1)
+          p = codes_bf16x8<1, FP8>(xv[i][j], s, 0.0f);
+        *reinterpret_cast<uint2*>(crow + c * 8) = p;
+        if (out_codes) *reinterpret_cast<uint2*>(qrow + c * 8) = p;
       }
     }
   }
-  __syncthreads();
-  if (t < 16 && t < M) srow[t] = __uint_as_float(amax_bits[t]) / kCodeMax<FP8>;
-  __syncthreads();
-  // codes into the LDS copy
-  int row = row0, pos = pos0;
-#pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    if (t + 256 * j < total) {
-      const float s = srow[row];
-      uint2 p = make_uint2(0u, 0u);
-      if (s >= kFastMinScale) {
-        p = codes_bf16x8<2, FP8>(xv[j], s, 1.0f / s);
-      } else if (s != 0.0f) {
-        p = codes_bf16x8<1, FP8>(xv[j], s, 0.0f);
-      }
-      *reinterpret_cast<uint2*>(codes + row * ldc + pos * 8) = p;
-      if (blockIdx.x == 0 && a.qx_out != nullptr)
-        *reinterpret_cast<uint2*>(a.qx_out + row * K + pos * 8) = p;
-    }
-    row += q256;
-    pos += r256;
-    if (pos >= ck) {
-      pos -= ck;
-      ++row;
-    }
-  }
-  if (blockIdx.x == 0 && a.sx_out != nullptr && t < M) a.sx_out[t] = srow[t];
   __syncthreads();
   // MFMAs over the wave's K share; rows past M read row M - 1 of the copy
   const int8_t* crow_l = codes + min<int64_t>(r, M - 1) * ldc;
@@ -1825,22 +1836,23 @@ hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
   return launch_few_rows_st<NW, NB, I32, STLOOP, true, FP8, MB, COAL>(a, stream);
 }
 
-template <int CH, int ST, bool FP8>
+template <int WPR, int RPW, int ST, bool FP8>
 hipError_t launch_linear_few_rows_st(const RowsArgs& a, hipStream_t stream) {
   const int64_t gx = (a.N + 15) / 16;
   if (gx > INT32_MAX) return hipErrorInvalidValue;
-  linear_few_rows<CH, ST, FP8><<<dim3(static_cast<unsigned>(gx)), dim3(256), 0, stream>>>(a);
+  linear_few_rows<WPR, RPW, ST, FP8><<<dim3(static_cast<unsigned>(gx)), dim3(256), 0, stream>>>(a);
   return hipGetLastError();
 }
 
-// Chunks of x per thread: CH covering M x K / 8 over 256 threads.
+// Rows over the 4 waves: 4 or 2 waves per row for 1 or 2 rows, else 1-3
+// rows per wave.
 template <int ST, bool FP8>
 hipError_t launch_linear_few_rows_ch(const RowsArgs& a, hipStream_t stream) {
-  const int64_t ch = (a.M * (a.K / 8) + 255) / 256;
-  if (ch <= 1) return launch_linear_few_rows_st<1, ST, FP8>(a, stream);
-  if (ch <= 2) return launch_linear_few_rows_st<2, ST, FP8>(a, stream);
-  if (ch <= 4) return launch_linear_few_rows_st<4, ST, FP8>(a, stream);
-  if (ch <= 6) return launch_linear_few_rows_st<6, ST, FP8>(a, stream);
+  if (a.M == 1) return launch_linear_few_rows_st<4, 1, ST, FP8>(a, stream);
+  if (a.M == 2) return launch_linear_few_rows_st<2, 1, ST, FP8>(a, stream);
+  if (a.M <= 4) return launch_linear_few_rows_st<1, 1, ST, FP8>(a, stream);
+  if (a.M <= 8) return launch_linear_few_rows_st<1, 2, ST, FP8>(a, stream);
+  if (a.M <= 12) return launch_linear_few_rows_st<1, 3, ST, FP8>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -2214,11 +2226,13 @@ hipError_t launch_gemm_gelu_amax(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The single-launch fused linear takes up to kRowsMaxM rows whose codes fit
-// the LDS copy (K <= 3072: at most 6 128-byte steps per wave), where the
-// library would run the few-row GEMM.
+// The single-launch fused linear takes up to kRowsMaxM rows (kRowsMaxMWide
+// above kNumCU column blocks) whose codes fit the LDS copy (K <= 3072: at
+// most 6 128-byte steps per wave), where the library would run the few-row
+// GEMM.
 bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K, bool fp8) {
   if (M < 1 || M > kRowsMaxM || N < 1 || K < 16 || K % 16 != 0 || K > kRowsMaxK) return false;
+  if (M > kRowsMaxMWide && (N + 15) / 16 > kNumCU) return false;
   return fp8 ? gemm_fp8_select_config(M, N, K) == kFp8FewRows
              : gemm_select_config(M, N, K) == kFewRows;
 }

@@ -33,6 +33,12 @@ __device__ __forceinline__ float absmax_of(u16x2 m) {
   const uint32_t b = m.x > m.y ? m.x : m.y;
   return __uint_as_float(b << 16);
 }
+// Maximum over the 64 lanes of a wave (every lane gets it; exact).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -67,12 +67,6 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-
 // Element c of a row through a 32-bit byte offset from the row's (scalar)
 // base, which lets the compiler use the scalar-base + vector-offset form.
 template <typename T>
