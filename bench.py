@@ -451,7 +451,8 @@ def compare(args, torch, w8, synthetic):
              quantization, then activations and weights dequantized to bf16
              and a bf16 GEMM (torch / hipBLASLt), bias added by the GEMM;
       bf16:  a plain bf16 GEMM on the unquantized bf16 weights.
-    Weight copies rotate past the 256 MB last-level cache for every leg."""
+    Weight copies rotate past the 256 MB last-level cache for every leg; the
+    legs are timed in 3 interleaved rounds (median over all their calls)."""
     import torch.nn.functional as F
     dev = "cuda:0"
     shapes = [s for k, v in synthetic.CONFIGS.items() if k != "unit" for s in v]
@@ -486,10 +487,18 @@ def compare(args, torch, w8, synthetic):
         def bf16(i):
             return F.linear(x, wbs[i], b)
 
-        t8 = _time_calls(torch, int8, args.sweep_iters, n8)
-        tf8 = _time_calls(torch, fp8, args.sweep_iters, n8)
-        tf = _time_calls(torch, fake, args.sweep_iters, n8)
-        tb = _time_calls(torch, bf16, args.sweep_iters, n16)
+        # the legs take turns: 3 rounds of sweep_iters calls each, the order
+        # reversed every other round, so that none of them is always timed
+        # first after the shape's setup (the chip's clock settles over a run)
+        legs = [("int8", int8, n8), ("fp8", fp8, n8), ("fake", fake, n8), ("bf16", bf16, n16)]
+        for _, fn, nc in legs:
+            for i in range(3):
+                fn(i % nc)
+        calls = {name: [] for name, _, _ in legs}
+        for rnd in range(3):
+            for name, fn, nc in (legs if rnd % 2 == 0 else legs[::-1]):
+                calls[name] += _call_times(torch, fn, args.sweep_iters, nc)
+        t8, tf8, tf, tb = ((_median(calls[n]), min(calls[n])) for n in ("int8", "fp8", "fake", "bf16"))
         int8(0)
         yf = fake(0)
         cos = F.cosine_similarity(y.float().flatten(), yf.float().flatten(), dim=0).item()
