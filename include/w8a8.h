@@ -131,8 +131,8 @@ size_t w8a8_linear_workspace_bytes(int64_t M, int64_t K);
  *   workspace  device memory of at least w8a8_linear_workspace_bytes(M, K),
  *              16-byte aligned; its contents on return are the codes and
  *              scales of x.  Calls sharing one workspace must be ordered.
- * For a few token rows (M <= 8, or M <= 12 with N <= 4096; K <= 3072) the
- * quantization, the GEMM and the epilogue run in one kernel launch.
+ * For a few token rows (M <= 16 with N <= 4096, M <= 12 above; K <= 3072)
+ * the quantization, the GEMM and the epilogue run in one kernel launch.
  * Source: the Abstract's fused INT8 GEMM that replaces the
  * dequantize-to-bf16 linear forward.
  */

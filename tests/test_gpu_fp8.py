@@ -252,12 +252,14 @@ def test_fp8_accumulation_error_calibration(K):
 # the e4m3 quantizer writes, and the same output bits as the two launches
 # (quantizer + the FP8 few-row GEMM) it replaces.  K tails that are not a
 # multiple of the 128-byte step, N not a multiple of 16, an all-zero row and
-# a subnormal-range row; every row split (4 or 2 waves per row, 1-3 rows per
-# wave); (16, 272, 2000) takes the two-launch path.
+# a subnormal-range row; every row split (4 waves: 4 or 2 waves per row or
+# one row per wave; 8 waves: one or two rows per wave); (13, 4112, 1040)
+# (more column blocks than CUs) takes the two-launch path.
 @pytest.mark.parametrize("M,N,K", [(1, 3072, 3072), (4, 3072, 3072), (3, 100, 1040), (3, 16, 16),
                                    (1, 18432, 3072), (2, 40, 48), (4, 272, 2000), (1, 16, 3072),
                                    (2, 3072, 3072), (6, 528, 1040), (8, 3072, 3072),
-                                   (9, 272, 2000), (12, 3072, 3072), (16, 272, 2000)])
+                                   (9, 272, 2000), (12, 3072, 3072), (16, 272, 2000),
+                                   (16, 3072, 3072), (13, 4112, 1040)])
 def test_linear_fp8_few_rows_single_launch(M, N, K):
     rng = np.random.default_rng(M * 1000 + K + N)
     xb = rand_bits(rng, M, K, outliers=max(1, K // 100))

@@ -424,16 +424,18 @@ def test_full_size_dit_block_chain():
 
 
 # A handful of token rows: w8a8_linear runs quantization, GEMM and epilogue in
-# one launch (up to 12 rows, K <= 3072; two launches for more rows) and
-# leaves the codes and scales in its workspace either way.  Every row split
-# of that kernel (4 or 2 waves per row, 1-3 rows per wave).  Rows include an
-# all-zero row and one whose scale is subnormal (the division path of the
-# quantizer), K with a ragged 64-element step, and N not a multiple of 16.
+# one launch (up to 16 rows with at most 256 column blocks, 12 with more; K <=
+# 3072) and leaves the codes and scales in its workspace either way; (13,
+# 4112, 1040) and (16, 18432, 3072) take the two launches.  Every row split of
+# that kernel (4 waves: 4 or 2 waves per row or one row per wave; 8 waves: one
+# or two rows per wave).  Rows include an all-zero row and one whose scale is
+# subnormal (the division path of the quantizer), K with a ragged 64-element
+# step, and N not a multiple of 16.
 @pytest.mark.parametrize("M,N,K", [(1, 3072, 3072), (4, 3072, 3072), (3, 100, 1040), (3, 16, 16),
                                    (1, 18432, 3072), (2, 40, 48), (4, 272, 2000), (1, 16, 3072),
                                    (2, 3072, 3072), (6, 528, 1040), (8, 3072, 3072),
                                    (12, 3072, 3072), (16, 3072, 3072), (9, 272, 2000),
-                                   (12, 18432, 3072)])
+                                   (12, 18432, 3072), (13, 4112, 1040), (16, 18432, 3072)])
 def test_few_rows_single_launch_linear_and_workspace(M, N, K):
     rng = np.random.default_rng(M * 100 + K + N)
     xb = rand_bits(rng, M, K, outliers=max(1, K // 100))

@@ -1641,14 +1641,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
 
 // ------------------------------------------- few tokens, fused quantize --
 // The whole fused linear for M <= 16 token rows in one launch.  Each
-// workgroup owns 16 output columns; its 4 waves split K for the MFMAs as in
-// gemm_few_rows.  Before them, the workgroup quantizes the M x K activations
-// itself, one wave per row as the row quantizer does (wave w takes rows w,
-// w + 4, ...): each lane loads 16-byte chunks lane, lane + 64, ... of the
-// row, the wave reduces the row's absmax with cross-lane maxima, and the
-// codes, computed with the row quantizer's own operations (quant_codes.h,
-// the same bits w8a8_quantize_act writes), go into an LDS copy of the codes;
-// each lane then reads its MFMA operand from there.  The activations are
+// workgroup owns 16 output columns; its 4 or 8 waves split K for the MFMAs
+// as in gemm_few_rows.  Before them, the workgroup quantizes the M x K
+// activations itself, one wave per row as the row quantizer does (wave w
+// takes rows w, w + NW, ...): each lane loads 16-byte chunks lane,
+// lane + 64, ... of the row, the wave reduces the row's absmax with
+// cross-lane maxima, and the codes, computed with the row quantizer's own
+// operations (quant_codes.h, the same bits w8a8_quantize_act writes), go
+// into an LDS copy of the codes; each lane then reads its MFMA operand from
+// there.  The activations are
 // loaded before the weight fragments (loads complete in issue order), so
 // they are quantized while the weights stream in.  Every workgroup reads all
 // of x (at most 16 x 3072 bf16, L2-resident after the first), in place of a
@@ -1660,13 +1661,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_few_rows(GemmArgs a) {
 constexpr int kRowsMaxK = 3072;  // codes of 16 rows of up to this K fit the LDS copy
 // Every workgroup quantizes all M rows, so the redundant work grows with M
 // and with the number of column blocks: the single launch is taken for up to
-// 8 rows, and up to 12 while there are no more column blocks than CUs
+// 16 rows while there are no more column blocks than CUs, up to 12 above
 // (measured against the two launches at K = 3072: M = 4, N = 3072 9.2 ->
-// 7.8 us, N = 18432 20.2 -> 16.9 us; M = 8 11.2 -> 9.3 and 20.8 -> 20.2 us;
-// M = 12, N = 3072 11.8 -> 11.0 us, but N = 18432 23.0 -> 23.4 us, and
-// M = 16 no faster at either N).
-constexpr int kRowsMaxM = 12;
-constexpr int kRowsMaxMWide = 8;  // above kNumCU column blocks
+// 7.8 us, N = 18432 20.2 -> 16.9 us; M = 8 11.2 -> 8.4 and 20.8 -> 19.6 us;
+// M = 12 11.8 -> 8.7 and 23.4 -> 21.8 us; M = 16, N = 3072 12.2 -> 10.5 us,
+// N = 18432 25.2 -> 25.1 us, FP8 24.3 -> 27.8 us).
+constexpr int kRowsMaxM = 16;
+constexpr int kRowsMaxMWide = 12;  // above kNumCU column blocks
 // K runs in 128-byte steps; lane l holds 32 bytes of row l % 16, K bytes
 // 32 (l / 16) .. +31 of a step (two 16-byte loads straight from the row).
 // int8: each step is two v_mfma_i32_16x16x64_i8, one on every lane's first
@@ -1678,19 +1679,22 @@ constexpr int kRowsMaxMWide = 8;  // above kNumCU column blocks
 // wave order; the weights are loaded and the pieces past K zeroed exactly as
 // the FP8 few-row GEMM does, so the output is the same bits as the two-launch
 // path (e4m3 quantizer + FP8 few-row GEMM).
-// Rows over waves: WPR waves share a row when M < 4 (WPR = 4 / M, each wave
-// a 64-lane slice of every 64 WPR chunks, maxima joined in LDS); otherwise
-// wave w takes rows w, w + 4, ... (RPW of them).  A row has at most 64 ST
-// chunks (ST: the 128-byte steps of a wave's K share, 512 ST >= K).
-template <int WPR, int RPW, int ST, bool FP8 = false>
-__global__ __launch_bounds__(256) void linear_few_rows(RowsArgs a) {
+// Rows over the NW waves: WPR waves share a row when there are fewer rows
+// than waves (each wave a 64-lane slice of every 64 WPR chunks, maxima
+// joined in LDS); otherwise wave w takes rows w, w + NW, ... (RPW of them).
+template <int WPR, int RPW, int ST, bool FP8 = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void linear_few_rows(RowsArgs a) {
   static_assert(WPR == 1 || RPW == 1, "shared rows: one per wave group");
-  constexpr int NW = 4;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int SB = 128;  // K bytes of one step
   constexpr int PB = 32;   // K bytes of one lane's operand in a step
-  constexpr int CHR = (ST + WPR - 1) / WPR;  // chunks of a row per lane
+  // chunks of a row per lane: NW ST 128-byte steps cover K, so a row's K / 8
+  // chunks are at most 64 ST NW / 4
+  constexpr int CHR = (ST * NW / 4 + WPR - 1) / WPR;
   using Acc = std::conditional_t<FP8, v4f, v4i>;
-  __shared__ __attribute__((aligned(16))) int8_t codes[16 * (kRowsMaxK + 16)];
+  constexpr int ROWS = NW / WPR * RPW;  // rows this launch shape holds (>= M)
+  static_assert(ROWS <= 16, "one 16-row MFMA block");
+  __shared__ __attribute__((aligned(16))) int8_t codes[ROWS * (kRowsMaxK + 16)];
   __shared__ Acc part[NW][64];
   __shared__ float srow[16];
   __shared__ float wmax[NW];
@@ -1870,23 +1874,31 @@ hipError_t launch_few_rows(const GemmArgs& a, hipStream_t stream) {
   return launch_few_rows_st<NW, NB, I32, STLOOP, true, FP8, MB, COAL>(a, stream);
 }
 
-template <int WPR, int RPW, int ST, bool FP8>
+template <int WPR, int RPW, int ST, bool FP8, int NW = 4>
 hipError_t launch_linear_few_rows_st(const RowsArgs& a, hipStream_t stream) {
   const int64_t gx = (a.N + 15) / 16;
   if (gx > INT32_MAX) return hipErrorInvalidValue;
-  linear_few_rows<WPR, RPW, ST, FP8><<<dim3(static_cast<unsigned>(gx)), dim3(256), 0, stream>>>(a);
+  linear_few_rows<WPR, RPW, ST, FP8, NW>
+      <<<dim3(static_cast<unsigned>(gx)), dim3(64 * NW), 0, stream>>>(a);
   return hipGetLastError();
 }
 
-// Rows over the 4 waves: 4 or 2 waves per row for 1 or 2 rows, else 1-3
-// rows per wave.
+// 4 waves for up to 4 rows (4 or 2 waves per row for 1 or 2 rows, else one
+// row per wave), 8 waves for 5-16 rows (one or two rows per wave, K in 8
+// shares): more waves hide more of the quantization's latency there, but at
+// 1-4 rows on wide N the 4-wave form measured faster (M = 1, N = 18432:
+// 14.6 against 15.5 us).
 template <int ST, bool FP8>
-hipError_t launch_linear_few_rows_ch(const RowsArgs& a, hipStream_t stream) {
+hipError_t launch_linear_few_rows_w4(const RowsArgs& a, hipStream_t stream) {
   if (a.M == 1) return launch_linear_few_rows_st<4, 1, ST, FP8>(a, stream);
   if (a.M == 2) return launch_linear_few_rows_st<2, 1, ST, FP8>(a, stream);
   if (a.M <= 4) return launch_linear_few_rows_st<1, 1, ST, FP8>(a, stream);
-  if (a.M <= 8) return launch_linear_few_rows_st<1, 2, ST, FP8>(a, stream);
-  if (a.M <= 12) return launch_linear_few_rows_st<1, 3, ST, FP8>(a, stream);
+  return hipErrorInvalidValue;
+}
+template <int ST, bool FP8>
+hipError_t launch_linear_few_rows_w8(const RowsArgs& a, hipStream_t stream) {
+  if (a.M <= 8) return launch_linear_few_rows_st<1, 1, ST, FP8, 8>(a, stream);
+  if (a.M <= 16) return launch_linear_few_rows_st<1, 2, ST, FP8, 8>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -2274,12 +2286,20 @@ bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K, bool fp8) {
 
 template <bool FP8>
 hipError_t launch_linear_few_rows_fmt(const RowsArgs& a, hipStream_t stream) {
-  const int64_t per = ((a.K + 127) / 128 + 3) / 4;  // 128-byte steps per wave
-  switch (per) {
-    case 1: return launch_linear_few_rows_ch<1, FP8>(a, stream);
-    case 2: return launch_linear_few_rows_ch<2, FP8>(a, stream);
-    case 3: case 4: return launch_linear_few_rows_ch<4, FP8>(a, stream);
-    case 5: case 6: return launch_linear_few_rows_ch<6, FP8>(a, stream);
+  const int64_t steps = (a.K + 127) / 128;  // 128-byte steps of K
+  if (a.M > 4) {
+    switch ((steps + 7) / 8) {  // per wave of 8
+      case 1: return launch_linear_few_rows_w8<1, FP8>(a, stream);
+      case 2: return launch_linear_few_rows_w8<2, FP8>(a, stream);
+      case 3: return launch_linear_few_rows_w8<3, FP8>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch ((steps + 3) / 4) {  // per wave of 4
+    case 1: return launch_linear_few_rows_w4<1, FP8>(a, stream);
+    case 2: return launch_linear_few_rows_w4<2, FP8>(a, stream);
+    case 3: case 4: return launch_linear_few_rows_w4<4, FP8>(a, stream);
+    case 5: case 6: return launch_linear_few_rows_w4<6, FP8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
