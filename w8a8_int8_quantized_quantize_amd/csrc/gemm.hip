@@ -1423,10 +1423,6 @@ __device__ __forceinline__ v4i to_mfma_layout(v4i v, int perm) {
   o[3] = __builtin_amdgcn_ds_bpermute(perm, v[3]);
   return o;
 }
-template <class F>
-__device__ __forceinline__ F to_mfma_layout(F v, int) {
-  return v;  // FP8 fragments keep the MFMA layout (no coalesced variant)
-}
 
 template <int NW, int NB, bool OUT_I32, int ST, bool LOOP, bool FP8 = false, int MB = 1,
           bool COAL = false, bool PIPE = false>
