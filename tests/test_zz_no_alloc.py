@@ -1,9 +1,10 @@
 """The allocation-free fused linear (w8a8_linear_noalloc), called through the
 C ABI: its output must equal w8a8_linear's (caller workspace) on the same
-inputs, element for element, and the oracle's, on two calls in a row, the
-second with a smaller input (the static scratch then still holds the first
-call's larger codes beyond the second's); a problem larger than the scratch
-is rejected with W8A8_ERR_SCRATCH before anything is enqueued."""
+inputs, element for element, and the oracle's, on calls in a row, each with a
+smaller input than the one before (the static scratch then still holds the
+earlier calls' larger codes beyond the current one's; the last call, 8 token
+rows, runs the single-launch few-row kernel); a problem larger than the
+scratch is rejected with W8A8_ERR_SCRATCH before anything is enqueued."""
 from __future__ import annotations
 
 import ctypes
@@ -37,7 +38,8 @@ def _call_noalloc(x, wq, sw, b, y):
 def test_noalloc_linear_matches_workspace_entry(order):
     assert w8.w8a8_linear_noalloc_max_bytes() == 64 << 20
     rng = np.random.default_rng(2024)
-    for M, N, K, with_bias in [(4096, 1536, 3072, True), (300, 520, 1040, False)]:
+    for M, N, K, with_bias in [(4096, 1536, 3072, True), (300, 520, 1040, False),
+                               (8, 3072, 3072, True)]:
         xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
         w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
         bb = rand_bits(rng, 1, N, scale=0.1)[0] if with_bias else None
