@@ -269,8 +269,8 @@ const char* w8a8_gemm_fp8_config_name(int config);
 /*
  * The fused FP8 linear: w8a8_quantize_act_fp8 of x into the workspace (same
  * size as w8a8_linear's: w8a8_linear_workspace_bytes(M, K)), then
- * w8a8_gemm_dequant_fp8.  w_q, s_w from w8a8_quantize_weight_fp8.  The same
- * few-row cases as w8a8_linear run in one launch (same output bits).
+ * w8a8_gemm_dequant_fp8.  w_q, s_w from w8a8_quantize_weight_fp8.  Up to 8
+ * token rows (K <= 3072) run in one launch, with the same output bits.
  */
 int w8a8_linear_fp8(const void* x_bf16, const uint8_t* w_q, const float* s_w,
                     const void* bias_bf16, int64_t M, int64_t N, int64_t K, void* y_bf16,

@@ -247,14 +247,13 @@ def test_fp8_accumulation_error_calibration(K):
 
 
 
-# The single-launch FP8 linear for a few token rows (e4m3 quantization, GEMM
+# The single-launch FP8 linear for up to 8 token rows (e4m3 quantization, GEMM
 # and epilogue in one kernel): the same codes and scales in the workspace as
 # the e4m3 quantizer writes, and the same output bits as the two launches
 # (quantizer + the FP8 few-row GEMM) it replaces.  K tails that are not a
 # multiple of the 128-byte step, N not a multiple of 16, an all-zero row and
-# a subnormal-range row; every row split (4 waves: 4 or 2 waves per row or
-# one row per wave; 8 waves: one or two rows per wave); (13, 4112, 1040)
-# (more column blocks than CUs) takes the two-launch path.
+# a subnormal-range row; every row split (4 or 2 waves per row, one or two
+# rows per wave); 9 rows and more take the two-launch path.
 @pytest.mark.parametrize("M,N,K", [(1, 3072, 3072), (4, 3072, 3072), (3, 100, 1040), (3, 16, 16),
                                    (1, 18432, 3072), (2, 40, 48), (4, 272, 2000), (1, 16, 3072),
                                    (2, 3072, 3072), (6, 528, 1040), (8, 3072, 3072),
@@ -283,3 +282,37 @@ def test_linear_fp8_few_rows_single_launch(M, N, K):
         y2 = w8.w8a8_gemm_dequant_fp8(q2, s2, wq, sw, bias)
         assert torch.equal(y, y2)
         assert_fp8_gemm_bound(bits(y), qx, sx, qw, swo, b_bits, f"linear_fp8 {M}x{N}x{K}")
+
+
+# The same, on weights whose rows each hold one value 1000x the rest: most
+# weight codes are then tiny e4m3 values next to one large one, so sums of the
+# products in fp32 round, and in an order-dependent way (checked here on the
+# host: two summation orders of the exact products give different fp32
+# results).  The single launch must still give the two-launch path's bits,
+# since both split K into the same 4 shares and add them in the same order.
+@pytest.mark.parametrize("M,N,K", [(1, 3072, 3072), (4, 272, 2000), (8, 3072, 3072)])
+def test_linear_fp8_single_launch_bits_where_fp32_sums_round(M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[np.arange(N), rng.integers(0, K, N)] *= np.float32(1000.0)
+    qx, sx = oracle.quantize_rows_bf16_fp8(xb)
+    qw, swo = oracle.quantize_rows_f32_fp8(w)
+    dx, dw = oracle.e4m3_decode(qx), oracle.e4m3_decode(qw)
+    fwd = np.zeros((M, N), np.float32)
+    bwd = np.zeros((M, N), np.float32)
+    for k in range(K):  # each product is exact in fp32 (two 4-bit significands)
+        fwd += (dx[:, k, None] * dw[None, :, k]).astype(np.float32)
+        kb = K - 1 - k
+        bwd += (dx[:, kb, None] * dw[None, :, kb]).astype(np.float32)
+    assert np.any(fwd != bwd)  # the data makes fp32 accumulation order-dependent
+    wq, sw = w8.w8a8_quantize_weight_fp8(torch.from_numpy(w).to(DEV))
+    assert np.array_equal(host(wq), qw)
+    x = dev_bf16(xb)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0]
+    b = dev_bf16(bb)
+    y = w8.w8a8_linear_fp8(x, wq, sw, b)
+    q2, s2 = w8.w8a8_quantize_act_fp8(x)
+    y2 = w8.w8a8_gemm_dequant_fp8(q2, s2, wq, sw, b)
+    assert torch.equal(y, y2)
+    assert_fp8_gemm_bound(bits(y), qx, sx, qw, swo, bb, f"linear_fp8 wide {M}x{N}x{K}")

@@ -1664,6 +1664,12 @@ constexpr int kRowsMaxK = 3072;  // codes of 16 rows of up to this K fit the LDS
 // N = 18432 25.2 -> 25.1 us, FP8 24.3 -> 27.8 us).
 constexpr int kRowsMaxM = 16;
 constexpr int kRowsMaxMWide = 12;  // above kNumCU column blocks
+// FP8: the fp32 partial sums of the K shares are added in wave order, so the
+// single launch gives the two-launch path's bits only with the same 4-wave K
+// split: 4 waves (two rows each above 4 rows), up to 8 rows (measured against
+// the two launches at K = 3072: M = 8, N = 3072 11.4 -> 9.9 us, N = 18432
+// 21.4 -> 21.0 us).
+constexpr int kRowsMaxMFp8 = 8;
 // K runs in 128-byte steps; lane l holds 32 bytes of row l % 16, K bytes
 // 32 (l / 16) .. +31 of a step (two 16-byte loads straight from the row).
 // int8: each step is two v_mfma_i32_16x16x64_i8, one on every lane's first
@@ -1880,15 +1886,16 @@ hipError_t launch_linear_few_rows_st(const RowsArgs& a, hipStream_t stream) {
 }
 
 // 4 waves for up to 4 rows (4 or 2 waves per row for 1 or 2 rows, else one
-// row per wave), 8 waves for 5-16 rows (one or two rows per wave, K in 8
-// shares): more waves hide more of the quantization's latency there, but at
+// row per wave), 8 waves for 5-16 int8 rows (one or two rows per wave, K in
+// 8 shares): more waves hide more of the quantization's latency there, but at
 // 1-4 rows on wide N the 4-wave form measured faster (M = 1, N = 18432:
-// 14.6 against 15.5 us).
+// 14.6 against 15.5 us).  FP8 keeps 4 waves (two rows each for 5-8 rows).
 template <int ST, bool FP8>
 hipError_t launch_linear_few_rows_w4(const RowsArgs& a, hipStream_t stream) {
   if (a.M == 1) return launch_linear_few_rows_st<4, 1, ST, FP8>(a, stream);
   if (a.M == 2) return launch_linear_few_rows_st<2, 1, ST, FP8>(a, stream);
   if (a.M <= 4) return launch_linear_few_rows_st<1, 1, ST, FP8>(a, stream);
+  if (FP8 && a.M <= kRowsMaxMFp8) return launch_linear_few_rows_st<1, 2, ST, FP8>(a, stream);
   return hipErrorInvalidValue;
 }
 template <int ST, bool FP8>
@@ -2274,7 +2281,9 @@ hipError_t launch_gemm_gelu_amax(const GemmArgs& a, hipStream_t stream) {
 // most 6 128-byte steps per wave), where the library would run the few-row
 // GEMM.
 bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K, bool fp8) {
-  if (M < 1 || M > kRowsMaxM || N < 1 || K < 16 || K % 16 != 0 || K > kRowsMaxK) return false;
+  if (M < 1 || M > (fp8 ? kRowsMaxMFp8 : kRowsMaxM) || N < 1 || K < 16 || K % 16 != 0 ||
+      K > kRowsMaxK)
+    return false;
   if (M > kRowsMaxMWide && (N + 15) / 16 > kNumCU) return false;
   return fp8 ? gemm_fp8_select_config(M, N, K) == kFp8FewRows
              : gemm_select_config(M, N, K) == kFewRows;
@@ -2283,7 +2292,7 @@ bool linear_few_rows_supported(int64_t M, int64_t N, int64_t K, bool fp8) {
 template <bool FP8>
 hipError_t launch_linear_few_rows_fmt(const RowsArgs& a, hipStream_t stream) {
   const int64_t steps = (a.K + 127) / 128;  // 128-byte steps of K
-  if (a.M > 4) {
+  if (a.M > 4 && !FP8) {
     switch ((steps + 7) / 8) {  // per wave of 8
       case 1: return launch_linear_few_rows_w8<1, FP8>(a, stream);
       case 2: return launch_linear_few_rows_w8<2, FP8>(a, stream);
