@@ -258,7 +258,8 @@ def test_fp8_accumulation_error_calibration(K):
                                    (1, 18432, 3072), (2, 40, 48), (4, 272, 2000), (1, 16, 3072),
                                    (2, 3072, 3072), (6, 528, 1040), (8, 3072, 3072),
                                    (9, 272, 2000), (12, 3072, 3072), (16, 272, 2000),
-                                   (16, 3072, 3072), (13, 4112, 1040), (12, 16, 16), (5, 48, 48)])
+                                   (16, 3072, 3072), (13, 4112, 1040), (12, 16, 16), (5, 48, 48),
+                                   (7, 40, 48)])
 def test_linear_fp8_few_rows_single_launch(M, N, K):
     rng = np.random.default_rng(M * 1000 + K + N)
     xb = rand_bits(rng, M, K, outliers=max(1, K // 100))

@@ -436,7 +436,8 @@ def test_full_size_dit_block_chain():
                                    (2, 3072, 3072), (6, 528, 1040), (8, 3072, 3072),
                                    (12, 3072, 3072), (16, 3072, 3072), (9, 272, 2000),
                                    (12, 18432, 3072), (13, 4112, 1040), (16, 18432, 3072),
-                                   (16, 272, 2000), (12, 16, 16), (5, 48, 48)])
+                                   (16, 272, 2000), (12, 16, 16), (5, 48, 48), (7, 40, 48),
+                                   (14, 100, 1040)])
 def test_few_rows_single_launch_linear_and_workspace(M, N, K):
     rng = np.random.default_rng(M * 100 + K + N)
     xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
