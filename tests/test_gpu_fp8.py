@@ -198,7 +198,7 @@ def test_full_size_linear_fp8(shape):
 
 
 @pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (4, 48), (4133, 3072),
-                                 (4500, 12288), (700, 10240)])
+                                 (4500, 12288), (700, 10240), (100, 8192), (37, 7008)])
 def test_gelu_quantize_fp8_teacher_forced(M, K):
     rng = np.random.default_rng(M + 5 * K)
     yb = rand_bits(rng, M, K, scale=3.0, outliers=max(1, K // 100))

@@ -89,12 +89,14 @@ def test_quantize_weight_bit_exact(N, K):
 
 
 # large M: the persistent grid of 256 workgroups x 16 waves (one row per wave
-# at a time) covers 4096 rows per pass; 4133, 4500 and 6000 take a second,
-# partial pass.  Long rows have fewer rows in flight per workgroup than waves
-# (8 at K = 12288, 10 at K = 10240): later rows wait for earlier ones to land
+# at a time) covers 4096 rows per pass; 4133 and 6000 take a second, partial
+# pass.  Rows of 13-24 chunks per lane (K 6152..12288) are split between two
+# waves, 8 rows per workgroup round: 4500 x 12288 takes a third, partial round
+# (pairs past M idle through its barrier), 700 x 10240 and 37 x 7008 halves
+# shorter than the per-lane chunk count, 100 x 8192 the 8-chunk halves.
 @pytest.mark.parametrize("M,K", [(64, 256), (33, 3072), (8, 12288), (2, 16384), (4, 48),
                                  (4133, 3072), (6000, 1040), (4096, 12288), (4500, 12288),
-                                 (700, 10240)])
+                                 (700, 10240), (100, 8192), (37, 7008)])
 def test_gelu_quantize_teacher_forced(M, K):
     rng = np.random.default_rng(M + 3 * K)
     yb = rand_bits(rng, M, K, scale=3.0, outliers=max(1, K // 100))

@@ -36,7 +36,8 @@
 // with direct-to-LDS loads.  One workgroup of 16 waves per CU (the table fills
 // 128 KiB of the 160 KiB of LDS); each element then costs one LDS gather.
 // A workgroup keeps a bounded number of rows in flight, so that rows land one
-// after another and their codes overlap the reads of later rows.
+// after another and their codes overlap the reads of later rows; rows longer
+// than 12 chunks per lane are split between two waves.
 //
 // Exactness: built with correctly rounded fp32 division, fp32 denormals kept
 // and contraction off, so every step matches the IEEE definition bit for bit.
@@ -372,6 +373,90 @@ __global__ __launch_bounds__(kLutThreads) void gelu_quantize_regs(
   }
 }
 
+// Long rows (13-24 chunks per lane: K up to 12288): two waves per row, wave
+// w and w + 8 taking its two halves, so that a wave has at most 12 loads in
+// flight (a streaming probe of 256 workgroups ran ~25% slower with 21-42
+// 16-byte loads per lane in flight than with 6-14).  The halves' maxima meet
+// in LDS, and the workgroup takes rows in rounds of 8 (one barrier each).
+// For 4096 rows of 12288: 33.8-34.0 us against 35.7-36.2 us for one wave per
+// row with 8 rows in flight.
+template <int CHH, bool FP8>
+__global__ __launch_bounds__(kLutThreads) void gelu_quantize_pairs(
+    const uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t ldy, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale, uint16_t* __restrict__ h_out) {
+  __shared__ __attribute__((aligned(1024))) uint16_t lut[65536];
+  __shared__ float pmax[2][kLutWaves];  // alternating rounds: no overwrite before a read
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int pair = wave % 8, half = wave / 8;
+  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  const uint32_t hch = (nch + 1) / 2;    // chunks of the first half (<= 64 CHH)
+  const uint32_t c0 = half * hch;        // this wave's first chunk
+  const uint32_t c1 = half ? nch : hch;  // one past its last (c1 > c0: nch >= 2)
+  stage_lut(lut);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  int par = 0;
+  // every wave runs the same rounds (the bound depends on the workgroup only)
+  for (int64_t base = (int64_t)blockIdx.x * 8; base < M; base += (int64_t)gridDim.x * 8, par ^= 1) {
+    const int64_t row = base + pair;
+    const bool active = row < M;  // wave-uniform
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    uint4 raw[CHH];
+    u16x2 m = {0, 0};
+    if (active) {
+      // chunks past the half's end are clamped to its last one (copies of
+      // real elements: the maximum is unchanged, their codes not stored)
+      const uint4* src = reinterpret_cast<const uint4*>(y + row * ldy);
+#pragma unroll
+      for (int j = 0; j < CHH; ++j) {
+        const uint32_t c = c0 + ln + 64u * j;
+        raw[j] = at(src, c < c1 ? c : c1 - 1);
+        __builtin_amdgcn_sched_barrier(0);  // issue order = chunk order
+      }
+      Gather8 cur;
+      cur.issue(lut, raw[0]);
+#pragma unroll
+      for (int j = 0; j < CHH; ++j) {
+        Gather8 nxt;
+        if (j + 1 < CHH) nxt.issue(lut, raw[j + 1]);  // next chunk's gathers in flight
+        raw[j] = cur.pack();
+        m = absmax2(absmax2(absmax2(absmax2(m, raw[j].x), raw[j].y), raw[j].z), raw[j].w);
+        cur = nxt;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const float hmax = wave_max(absmax_of(m));
+    if (lane == 0) pmax[par][wave] = hmax;
+    __syncthreads();
+    if (!active) continue;
+    // the row's scale and quotient mode, as row_scale computes them
+    const float s = fmaxf(pmax[par][pair], pmax[par][pair + 8]) / kCodeMax<FP8>;
+    float r = 0.0f;
+    const int mode = s == 0.0f ? 0 : (s >= kFastMinScale ? 2 : 1);
+    if (mode == 2) r = 1.0f / s;
+    if (lane == 0 && half == 0) scale[row] = s;
+    if (h_out != nullptr) {
+      uint4* hrow = reinterpret_cast<uint4*>(h_out + row * K);
+#pragma unroll
+      for (int j = 0; j < CHH; ++j) {
+        const uint32_t c = c0 + ln + 64u * j;
+        if (c < c1) at(hrow, c) = raw[j];
+      }
+    }
+    uint2* dst = reinterpret_cast<uint2*>(q + row * ldq);
+#pragma unroll
+    for (int j = 0; j < CHH; ++j) {
+      const uint32_t c = c0 + ln + 64u * j;
+      if (c < c1)
+        at(dst, c) = mode == 2 ? codes_bf16x8<2, FP8>(raw[j], s, r)
+                               : (mode == 1 ? codes_bf16x8<1, FP8>(raw[j], s, r)
+                                            : make_uint2(0u, 0u));
+    }
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(kLutThreads) void gelu_quantize_loop(
     const uint16_t* __restrict__ y, int64_t M, int64_t K, int64_t ldy, int8_t* __restrict__ q,
@@ -482,11 +567,11 @@ hipError_t launch_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
   return hipGetLastError();
 }
 
-// Rows per GELU workgroup in flight: about 192 KiB of row data per compute
-// unit, at least 4 rows and at most one per wave.  For K = 12288 that is 8
-// rows: on MI355X, 4096 such rows take 31.9 us with 8 in flight against
-// 34.3 us with all 16 (one row per wave, all loads at once) and 32.0-34.4 us
-// with 3, 4 or 6.
+// Rows per GELU workgroup in flight (one wave per row, rows of up to 12
+// chunks per lane): about 192 KiB of row data per compute unit, at least 4
+// rows and at most one per wave.  (When K = 12288 rows took this kernel, 8
+// in flight measured 31.9 us for 4096 rows against 34.3 us with all 16 and
+// 32.0-34.4 us with 3, 4 or 6.)
 int gelu_rows_in_flight(int64_t K) {
   const int64_t row_bytes = 2 * K;
   const int64_t d = (192 * 1024 + row_bytes - 1) / row_bytes;
@@ -506,8 +591,18 @@ hipError_t launch_gelu(const uint16_t* y, int64_t M, int64_t K, int64_t ldy, int
         <<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out, depth);            \
     return hipGetLastError();                                                                \
   }
-  W8A8_FOR_CH(W8A8_G_CASE)
+  W8A8_G_CASE(1) W8A8_G_CASE(2) W8A8_G_CASE(3) W8A8_G_CASE(4) W8A8_G_CASE(6) W8A8_G_CASE(8)
+  W8A8_G_CASE(12)
 #undef W8A8_G_CASE
+  if (per_lane <= 24) {
+    // two waves per row, rows in rounds of 8 per workgroup
+    const dim3 grid2(static_cast<unsigned>(std::min<int64_t>((M + 7) / 8, kLutMaxBlocks)));
+    if (per_lane <= 16)
+      gelu_quantize_pairs<8, FP8><<<grid2, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out);
+    else
+      gelu_quantize_pairs<12, FP8><<<grid2, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out);
+    return hipGetLastError();
+  }
   gelu_quantize_loop<FP8><<<grid, block, 0, stream>>>(y, M, K, ldy, q, ldq, scale, h_out);
   return hipGetLastError();
 }
