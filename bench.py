@@ -520,9 +520,9 @@ def main():
         write_traffic(*args.traffic_from)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the layer shards over tokens or output channels without communication; see the "
-              f"design notes).", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer "
+              f"would shard over tokens or output channels, with no communication between GPUs).",
+              file=sys.stderr)
         return 2
 
     import torch

@@ -322,7 +322,7 @@ def test_int_mm_cross_check_where_available():
     b = torch.from_numpy(rng.integers(-127, 128, (N, K)).astype(np.int8)).to(DEV)
     try:
         ref = torch._int_mm(a, b.t().contiguous())
-    except Exception as e:  # not supported on this build / shape
+    except Exception as e:  # not supported by this PyTorch or shape
         pytest.skip(f"torch._int_mm unavailable: {e}")
     assert torch.equal(w8.w8a8_gemm_i32(a, b), ref)
 
