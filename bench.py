@@ -70,7 +70,7 @@ def parse():
                          "row absmax folded into the up-projection's epilogue + an absmax-given quantizer")
     ap.add_argument("--profile-shapes", default="",
                     help="comma-separated workload shape names: run the fused linear (w8a8_linear) "
-                         "on each, --iters times, weights rotated (a driver for rocprofv3 counters)")
+                         "on each, --iters times, weights rotated (a workload for rocprofv3 counter runs)")
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of known size (counter calibration)")

@@ -8,7 +8,7 @@
 * The CPU oracle (oracle/oracle.c) with the same sanitizers, driven by
   tests/csrc/oracle_host_check.c on small strided inputs and its edge cases.
 
-Both drivers exit 0 only if every check holds and no sanitizer reports.
+Both check programs exit 0 only if every check holds and no sanitizer reports.
 """
 from __future__ import annotations
 
