@@ -63,7 +63,8 @@ def assert_fp8_gemm_bound(y_bits, q_x, s_x, q_w, s_w, bias_bits, what="", sums=N
     return float(np.mean(y_bits != want))
 
 
-@pytest.mark.parametrize("M,K", [(1, 16), (7, 48), (33, 1040), (64, 256), (257, 3072), (5, 12288)])
+@pytest.mark.parametrize("M,K", [(1, 16), (7, 48), (33, 1040), (64, 256), (257, 3072), (5, 12288),
+                                 (300, 8192)])
 def test_quantize_act_fp8_bit_exact(M, K):
     rng = np.random.default_rng(M * 13 + K)
     xb = rand_bits(rng, M, K, outliers=max(1, K // 100))

@@ -44,8 +44,10 @@ def rand_bits(rng, M, K, scale=1.0, outliers=0):
 
 
 # ------------------------------------------------------------ quantization --
+# (rows of 13-24 chunks per lane, K 6152..12288, are split between two waves:
+# 5 x 12288, 3000 x 8192 and 7 x 10240, whose halves are shorter than 12 chunks)
 QSHAPES = [(1, 16), (7, 48), (33, 1040), (64, 256), (257, 3072), (5, 12288), (3, 16384),
-           (2, 24592), (1, 133136)]
+           (2, 24592), (1, 133136), (3000, 8192), (7, 10240)]
 
 
 @pytest.mark.parametrize("M,K", QSHAPES)

@@ -167,6 +167,67 @@ __global__ __launch_bounds__(kThreads) void quantize_bf16_regs(
   }
 }
 
+// Long rows (13-24 chunks per lane: K up to 12288): two waves per row (the
+// workgroup's waves w and w + 2 take its row w's two halves), so that a wave
+// has at most 12 loads per lane in flight; the halves' maxima meet in LDS.
+template <int CHH, bool FP8>
+__global__ __launch_bounds__(kThreads) void quantize_bf16_halves(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
+    int64_t ldq, float* __restrict__ scale) {
+  constexpr int R = kWaves / 2;  // rows per workgroup and round
+  __shared__ float hmax[2][kWaves];  // alternating rounds: no overwrite before a read
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int slot = wave % R, half = wave / R;
+  const uint32_t nch = static_cast<uint32_t>(K / 8);
+  const uint32_t hch = (nch + 1) / 2;    // chunks of the first half (<= 64 CHH)
+  const uint32_t c0 = half * hch;        // this wave's first chunk
+  const uint32_t c1 = half ? nch : hch;  // one past its last (c1 > c0: nch >= 2)
+  int par = 0;
+  // every wave runs the same rounds (the bound depends on the workgroup only)
+  for (int64_t base = (int64_t)blockIdx.x * R; base < M; base += (int64_t)gridDim.x * R, par ^= 1) {
+    const int64_t row = base + slot;
+    const bool active = row < M;  // wave-uniform
+    uint32_t ln = lane;            // opaque per row: keeps per-chunk indices
+    asm volatile("" : "+v"(ln));   // from being hoisted into live registers
+    uint4 raw[CHH];
+    u16x2 m = {0, 0};
+    if (active) {
+      // chunks past the half's end are clamped to its last one (copies of
+      // real elements: the maximum is unchanged, their codes not stored)
+      const uint4* src = reinterpret_cast<const uint4*>(x + row * ldx);
+#pragma unroll
+      for (int j = 0; j < CHH; ++j) {
+        const uint32_t c = c0 + ln + 64u * j;
+        raw[j] = at(src, c < c1 ? c : c1 - 1);
+        __builtin_amdgcn_sched_barrier(0);  // issue order = chunk order
+      }
+#pragma unroll
+      for (int j = 0; j < CHH; ++j)
+        m = absmax2(absmax2(absmax2(absmax2(m, raw[j].x), raw[j].y), raw[j].z), raw[j].w);
+    }
+    const float wm = wave_max(absmax_of(m));
+    if (lane == 0) hmax[par][wave] = wm;
+    __syncthreads();
+    if (!active) continue;
+    // the row's scale and quotient mode, as row_scale computes them
+    const float s = fmaxf(hmax[par][slot], hmax[par][slot + R]) / kCodeMax<FP8>;
+    float r = 0.0f;
+    const int mode = s == 0.0f ? 0 : (s >= kFastMinScale ? 2 : 1);
+    if (mode == 2) r = 1.0f / s;
+    if (lane == 0 && half == 0) scale[row] = s;
+    uint2* dst = reinterpret_cast<uint2*>(q + row * ldq);
+#pragma unroll
+    for (int j = 0; j < CHH; ++j) {
+      const uint32_t c = c0 + ln + 64u * j;
+      if (c < c1)
+        at(dst, c) = mode == 2 ? codes_bf16x8<2, FP8>(raw[j], s, r)
+                               : (mode == 1 ? codes_bf16x8<1, FP8>(raw[j], s, r)
+                                            : make_uint2(0u, 0u));
+    }
+  }
+}
+
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void quantize_bf16_loop(
     const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, int8_t* __restrict__ q,
@@ -561,8 +622,18 @@ hipError_t launch_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int
     quantize_bf16_regs<CHV, FP8><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale); \
     return hipGetLastError();                                                             \
   }
-  W8A8_FOR_CH(W8A8_Q_CASE)
+  W8A8_Q_CASE(1) W8A8_Q_CASE(2) W8A8_Q_CASE(3) W8A8_Q_CASE(4) W8A8_Q_CASE(6) W8A8_Q_CASE(8)
+  W8A8_Q_CASE(12)
 #undef W8A8_Q_CASE
+  if (K > 0 && per_lane <= 24) {
+    // two waves per row, two rows per workgroup and round
+    const dim3 grid2(static_cast<unsigned>(std::min<int64_t>((M + 1) / 2, kMaxBlocks)));
+    if (per_lane <= 16)
+      quantize_bf16_halves<8, FP8><<<grid2, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
+    else
+      quantize_bf16_halves<12, FP8><<<grid2, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
+    return hipGetLastError();
+  }
   quantize_bf16_loop<FP8><<<grid, block, 0, stream>>>(x, M, K, ldx, q, ldq, scale);
   return hipGetLastError();
 }
