@@ -110,6 +110,13 @@ def test_config_selection_table():
             c = w8.w8a8_gemm_select_config(s.M, s.N, s.K)
             assert 0 <= c < n, s
     assert w8.w8a8_gemm_select_config(0, 4, 16) == -1
+    # the 256 x 384 ping-pong tile: the measured choice for the 1024px
+    # up-projection; the cost model takes it only for shapes of whole tiles
+    wide = names.index("bm256_bn384_bk64_s3_mf16_pp")
+    assert w8.w8a8_gemm_select_config(4096, 12288, 3072) == wide
+    assert w8.w8a8_gemm_select_config(8192, 12288, 3072) == wide
+    assert w8.w8a8_gemm_select_config(8192, 12160, 3072) != wide   # N not a multiple of 384
+    assert w8.w8a8_gemm_select_config(8192, 12288, 3000) != wide   # K not a multiple of 64
 
 
 def test_fp8_entry_validation():

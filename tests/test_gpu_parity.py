@@ -232,6 +232,31 @@ def test_consecutive_interior_tiles_every_config(M, N, K):
         assert np.array_equal(bits(yc), yo), w8.w8a8_gemm_config_name(c)
 
 
+# The 256 x 384 ping-pong tile (configuration 14) on shapes of whole tiles:
+# one tile at the minimum depth (3 stages, K = 192), four tiles, 216 tiles
+# (one per workgroup, the 768px QKV projection's grid at a short K) and 432
+# tiles at K = 192 (workgroups chain tiles whose K loop is no longer than
+# the pipeline), each bit-exact against the oracle with and without a bias.
+@pytest.mark.parametrize("M,N,K", [(256, 384, 192), (512, 768, 256), (2304, 9216, 320),
+                                   (4608, 9216, 192)])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_wide_pingpong_tile_whole_tiles(M, N, K, with_bias):
+    rng = np.random.default_rng(M + N + K + with_bias)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0] if with_bias else None
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    wqo, swo = oracle.quantize_rows_f32(w)
+    assert np.array_equal(host(wq), wqo) and np.array_equal(host(sw), swo)
+    want = oracle.linear(xb, wqo, swo, bb)["y"]
+    q, s = w8.w8a8_quantize_act(dev_bf16(xb))
+    bias = dev_bf16(bb) if with_bias else None
+    cfg = [c for c in range(ncfg()) if w8.w8a8_gemm_config_name(c) == "bm256_bn384_bk64_s3_mf16_pp"]
+    assert len(cfg) == 1
+    y = w8.w8a8_gemm_ex(q, s, wq, sw, bias, config=cfg[0])
+    assert np.array_equal(bits(y), want)
+
+
 def _at_offset(t: torch.Tensor, k: int) -> torch.Tensor:
     """A copy of 1-D t that starts k elements into a fresh allocation."""
     big = torch.zeros(t.numel() + k, dtype=t.dtype, device=DEV)

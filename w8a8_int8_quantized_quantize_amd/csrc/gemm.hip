@@ -191,7 +191,10 @@ struct Tile {
   // wave must issue the same number per stage; 2-stage pipelines wait for 0
   static_assert(STAGES == 2 || kLoads % kWaves == 0, "uneven loads need a 2-stage pipeline");
   static_assert(STAGES >= 2 && STAGES * kStage + kEpiBytes <= 160 * 1024, "LDS budget");
-  static_assert(!kEpiLds || kWaves >= 3, "three waves load the epilogue's vectors");
+  // one 1 KiB load per wave: s_w on wave 0 (and wave 3 past 256 columns),
+  // s_x on wave 1, the bias on wave 2
+  static_assert(!kEpiLds || (kWaves >= (BN * 4 > 1024 ? 4 : 3) && BN * 4 <= 2048 && BM * 4 <= 1024),
+                "epilogue vectors: one load per wave");
 };
 
 // Store instructions one wave of the interior-tile bf16 epilogue issues: one
@@ -870,7 +873,11 @@ __device__ __forceinline__ void stage_epilogue_vectors(const GemmArgs& a, int8_t
   int bytes = 0, dst = 0;
   if (wave == 0) {
     src = reinterpret_cast<const int8_t*>(a.sw + n0);
-    bytes = C::BN * 4;
+    bytes = C::BN * 4 > 1024 ? 1024 : C::BN * 4;
+  } else if (C::BN * 4 > 1024 && wave == 3) {
+    src = reinterpret_cast<const int8_t*>(a.sw + n0) + 1024;
+    bytes = C::BN * 4 - 1024;
+    dst = 1024;
   } else if (wave == 1) {
     src = reinterpret_cast<const int8_t*>(a.sx + m0);
     bytes = C::BM * 4;
@@ -1260,9 +1267,10 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(GemmArgs a, int T, in
 // Loads and stores of a wave retire in issue order; a wave's loads of stage
 // i + 1 are followed by the refills of S - 2 later steps (L loads each), and
 // for the first S - 2 steps of a tile also by the previous tile's epilogue
-// stores, which fixes each wait count at compile time.  (Waves 0-2 also load
-// the tile's epilogue vectors at step 0, one load each, after those stages:
-// their waits then cover one load more than needed.)  The refills of a
+// stores, which fixes each wait count at compile time.  (Waves 0-2, and 3
+// on 384-column tiles, also load the tile's epilogue vectors at step 0, one
+// load each, after those stages: their waits then cover one load more than
+// needed.)  The refills of a
 // tile's last S - 1 steps load the workgroup's next tile's first stages
 // (consecutive tiles chain, so a tile needs K >= S x BK), or repeat the last
 // stage after the workgroup's last tile.  The epilogue vectors (scales, bias)
@@ -1930,6 +1938,7 @@ using C7 = Tile<256, 192, 2, 2, 64, 4, 32>;   // wave tile 128(m) x 96(n)
 using C9 = Tile<256, 256, 2, 2, 64, 4, 16>;   // C0 on 16x16x64 blocks, one k-step per stage
 using C10 = Tile<256, 192, 2, 2, 64, 4, 16>;  // C7 on 16x16x64 blocks
 using C11 = Tile<256, 256, 2, 4, 64, 4, 16>;  // C9 with 8 waves (2 per SIMD), wave tile 128 x 64
+using C14 = Tile<256, 384, 2, 4, 64, 3, 16>;  // 8 waves, wave tile 128 x 96, 3 stages of 40 KiB
 // configuration 12: C11's tile on the ping-pong kernel (gemm_pp_kernel) for
 // interior tiles; its edge tiles, and shapes with K < STAGES x BK, take C11's
 // own kernels
@@ -1938,6 +1947,14 @@ using C11 = Tile<256, 256, 2, 4, 64, 4, 16>;  // C9 with 8 waves (2 per SIMD), w
 // on a 256 x 3072 output, where the tiled kernels' large tiles would leave
 // most CUs idle; each wave's K share runs one 64-byte step at a time with
 // the next step's loads in flight (PIPE)
+// configuration 14: the ping-pong kernel on 256 x 384 tiles (C14): each
+// wave's 128 x 96 accumulator tile reads 22% fewer LDS bytes per MFMA than
+// C11's 128 x 64 (224 against 192 bytes of fragments for 48 against 32
+// MFMAs per k-step), and a tile loads 17% fewer operand bytes per operation;
+// it fills the 256 registers two waves per SIMD allow.  Shapes of whole
+// tiles (M a multiple of 256, N of 384, K of 64 with at least 3 stages,
+// aligned vectors) with bf16 output; anything else, int32 output included,
+// takes configuration 12's path.
 
 const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 0.97f},
@@ -1954,11 +1971,13 @@ const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf16_w8", 256, 256, 512, 1, 0.99f},
     {"bm256_bn256_bk64_s4_mf16_pp", 256, 256, 512, 1, 1.05f},
     {"rows64_bn48_splitk8_mf16", 64, 48, 512, 1, 0.30f},
+    {"bm256_bn384_bk64_s3_mf16_pp", 256, 384, 512, 1, 1.14f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kSkinny = 6;    // 16-row tiled kernel
 constexpr int kFewRows = 8;   // split-K few-row kernel
 constexpr int kRowBlocks = 13;  // split-K kernel on 64-row blocks
+constexpr int kPpWide = 14;     // 256 x 384 ping-pong tile, whole tiles only
 constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
 // Persistent grid: as many workgroups of `kernel` as fit on the device at
@@ -2077,6 +2096,30 @@ hipError_t launch_pp(const GemmArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
+// Whole 256 x 384 tiles for the wide ping-pong configuration (vector
+// alignment is checked at launch).
+bool pp_wide_covers(int64_t M, int64_t N, int64_t K) {
+  return M > 0 && N > 0 && M % C14::BM == 0 && N % C14::BN == 0 && K % C14::BK == 0 &&
+         K / C14::BK >= C14::STAGES;
+}
+
+// Configuration 14, bf16 output: the wide ping-pong tile when it covers the
+// shape, else configuration 12's path (same output bits either way).
+hipError_t launch_pp_wide(const GemmArgs& a, hipStream_t stream) {
+  const bool aligned = reinterpret_cast<uintptr_t>(a.sw) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(a.sx) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(a.bias) % 16 == 0;
+  if (!aligned || !pp_wide_covers(a.M, a.N, a.K)) return launch_pp<C11, false>(a, stream);
+  const int64_t MTi = a.M / C14::BM, NTi = a.N / C14::BN, Ti = MTi * NTi;
+  if (Ti > INT32_MAX) return hipErrorInvalidValue;
+  int grid = 0;
+  hipError_t e = persistent_grid<gemm_pp_kernel<C14, false>>(C14::kThreads, Ti, grid);
+  if (e != hipSuccess) return e;
+  gemm_pp_kernel<C14, false><<<dim3(grid), dim3(C14::kThreads), 0, stream>>>(
+      a, static_cast<int>(Ti), static_cast<int>(MTi), static_cast<int>(NTi));
+  return hipGetLastError();
+}
+
 template <class C>
 hipError_t launch_cfg_out(const GemmArgs& a, bool i32, hipStream_t stream) {
   return i32 ? launch_cfg<C, true>(a, stream) : launch_cfg<C, false>(a, stream);
@@ -2112,8 +2155,8 @@ struct MeasuredChoice {
 const MeasuredChoice kMeasured[] = {
     {64, 128, 256, 8},         // unit: few_rows_splitk4_mf16
     {2304, 3072, 3072, 3},     // 768px attention projection: bm128_bn256_bk128_s3_mf32
-    {2304, 9216, 3072, 10},    // 768px fused QKV: bm256_bn192_bk64_s4_mf16
-    {4096, 12288, 3072, 12},   // 1024px MLP up: bm256_bn256_bk64_s4_mf16_pp
+    {2304, 9216, 3072, 14},    // 768px fused QKV: bm256_bn384_bk64_s3_mf16_pp
+    {4096, 12288, 3072, 14},   // 1024px MLP up: bm256_bn384_bk64_s3_mf16_pp
     {4096, 3072, 12288, 10},   // 1024px MLP down: bm256_bn192_bk64_s4_mf16
     {1, 18432, 3072, 8},       // few_rows_splitk4_mf16
     {1, 3072, 3072, 8},
@@ -2121,10 +2164,11 @@ const MeasuredChoice kMeasured[] = {
     {16, 3072, 3072, 8},
     {256, 18432, 3072, 2},     // bm256_bn128_bk128_s3_mf32
     {256, 3072, 3072, 13},     // rows64_bn48_splitk8_mf16
-    {4608, 9216, 3072, 12},    // 1024px block chain: the ping-pong tile, except the
-    {4608, 3072, 3072, 12},    // down-projection, where the 8-wave generic tile was faster
-    {4608, 12288, 3072, 12},   // in three interleaved rounds of 100 calls (162-164 against
-    {4608, 3072, 12288, 11},   // 165-167 us)
+    {4608, 9216, 3072, 14},    // 1024px block chain: the wide ping-pong tile on the QKV
+    {4608, 3072, 3072, 12},    // projection, the 256 x 256 one on the out- and up-projections
+    {4608, 12288, 3072, 12},   // (576 wide tiles fill 2.25 rounds of the CUs: a tie), and the
+    {4608, 3072, 12288, 11},   // 8-wave generic tile on the down-projection, faster in three
+                               // interleaved rounds of 100 calls (162-164 against 165-167 us)
 };
 const MeasuredChoice kFp8Measured[] = {
     {64, 128, 256, 3},         // fp8_few_rows_splitk4_mf16
@@ -2159,6 +2203,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   for (int c = 0; c < kNumConfigs; ++c) {
     if (c == kSkinny || c == kFewRows) continue;  // chosen above for M <= 16
     if (c == kRowBlocks) continue;  // measured choice only
+    if (c == kPpWide && !pp_wide_covers(M, N, K)) continue;  // else configuration 12's path
     const ConfigInfo& ci = kConfigs[c];
     const int64_t tiles = ((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
     // workgroups resident on one CU share its matrix-core throughput
@@ -2331,6 +2376,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 12: return out_int32 ? launch_pp<C11, true>(a, stream) : launch_pp<C11, false>(a, stream);
     case 13: return out_int32 ? launch_few_rows_st<8, 3, true, 1, false, false, 4, true, true>(a, stream)
                               : launch_few_rows_st<8, 3, false, 1, false, false, 4, true, true>(a, stream);
+    case 14: return out_int32 ? launch_pp<C11, true>(a, stream) : launch_pp_wide(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
