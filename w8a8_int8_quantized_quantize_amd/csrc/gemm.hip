@@ -2138,15 +2138,19 @@ const char* gemm_config_name(int cfg) {
 // x (workgroups sharing a CU) / (relative per-CU throughput).  Workgroups
 // share a CU only when there are more tiles than CUs: with fewer, each tile
 // has a CU to itself and small tiles finish sooner.  A handful of
-// tokens (M <= 16) takes the split-K few-row kernel, except a nearly full
-// 16-row block with enough 64-column tiles to give every CU one: there the
-// 16-row tiled kernel, which shares the activations of a tile through LDS,
-// streams the weights faster.
+// tokens (M <= 16) takes the split-K few-row kernel (also with 16 rows and
+// enough 64-column tiles to give every CU one, where the 16-row tiled kernel
+// was the faster one before the few-row kernel's coalesced loads: 21.2
+// against 23.7 us on 16 x 18432 x 3072).
 // Measured choices for the workload shapes: the fastest configuration of a
 // full sweep on MI355X (bench.py --sweep, median of 20 calls on the shape's
-// own seeded codes, weights rotated past the last-level cache).  Other shapes
-// take the cost model below, which picks the same configuration as the sweep
-// on 12 of these 15 shapes (the other three within 3.4%).
+// own seeded codes, weights rotated past the last-level cache), with close
+// calls settled by interleaved rounds.  Other shapes take the cost model
+// below, which on these 15 shapes picks the measured choice on 11, is within
+// 1.6% of it on one (the 4608-token down-projection) and 3.1-3.3% on two (the
+// 64 x 128 x 256 unit shape, the 768px attention projection), and misses the
+// 256 x 3072 shape by 22%, whose 64-row split-K configuration is a measured
+// choice only.
 namespace {
 struct MeasuredChoice {
   int64_t M, N, K;
@@ -2194,10 +2198,7 @@ int measured_choice(const MeasuredChoice (&t)[N], int64_t M, int64_t Nn, int64_t
 
 int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   if (int c = measured_choice(kMeasured, M, N, K); c >= 0) return c;
-  if (M <= 16) {
-    const int64_t tiles = (N + kConfigs[kSkinny].BN - 1) / kConfigs[kSkinny].BN;
-    return (M > 12 && tiles >= kNumCU) ? kSkinny : kFewRows;
-  }
+  if (M <= 16) return kFewRows;
   int best = 0;
   double best_cost = 1e300;
   for (int c = 0; c < kNumConfigs; ++c) {
