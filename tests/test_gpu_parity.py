@@ -137,10 +137,13 @@ def test_gelu_quantize_every_finite_bf16_pattern():
 # (600, 700, 1024): K a whole number of stages with ragged M and N, so that
 # every tiled configuration runs both its interior-tile and edge-tile kernels;
 # (520, 530, 256) and (520, 530, 128): interior tiles with no more K stages
-# than LDS buffers (their epilogue vectors are waited for explicitly)
+# than LDS buffers (their epilogue vectors are waited for explicitly);
+# (300, 768, 256) and (512, 768, 128): N a multiple of the 384-column tile but
+# M ragged, or K shorter than its 3 stages, which the 256 x 384 ping-pong
+# configuration hands to the 256 x 256 one
 GSHAPES = [(64, 128, 256), (300, 520, 1040), (1, 16, 16), (7, 48, 48), (33, 272, 4112),
            (257, 16, 16), (16, 1000, 3072), (129, 257, 144), (3, 200, 12304), (600, 700, 1024),
-           (520, 530, 256), (520, 530, 128)]
+           (520, 530, 256), (520, 530, 128), (300, 768, 256), (512, 768, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", GSHAPES)
