@@ -1350,12 +1350,22 @@ __global__ __launch_bounds__(C::kThreads) void gemm_pp_kernel(GemmArgs a, int T,
       {
         const int rs = i + S - 1;  // refill: stage rs, into the buffer stage i - 1 used
         int8_t* dst = smem + ((ph + rs) % S) * C::kStage;
-        if (rs < KST)
-          ld.template issue_part_at<0, L>(n0, m0, rs, dst, wv, ln);
-        else if (more)
-          ld.template issue_part_at<0, L>(n1, m1, rs - KST, dst, wv, ln);
-        else
-          ld.template issue_part_at<0, L>(n0, m0, KST - 1, dst, wv, ln);
+        if constexpr (C::BN > 256) {
+          // one call site (scalar selects): on the 256 x 384 tile the three
+          // cases' load addresses overflowed the scalar registers, and the
+          // spill's reload made the compiler drain every load at each tile's
+          // first k-steps
+          const bool own = rs < KST, nxt = !own && more;
+          ld.template issue_part_at<0, L>(nxt ? n1 : n0, nxt ? m1 : m0,
+                                          own ? rs : (nxt ? rs - KST : KST - 1), dst, wv, ln);
+        } else {
+          if (rs < KST)
+            ld.template issue_part_at<0, L>(n0, m0, rs, dst, wv, ln);
+          else if (more)
+            ld.template issue_part_at<0, L>(n1, m1, rs - KST, dst, wv, ln);
+          else
+            ld.template issue_part_at<0, L>(n0, m0, KST - 1, dst, wv, ln);
+        }
       }
       const bool xst = stored && i <= S - 3;  // previous epilogue's stores after stage i + 1
       if (grp == 1) {
