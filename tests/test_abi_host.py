@@ -117,6 +117,12 @@ def test_config_selection_table():
     assert w8.w8a8_gemm_select_config(8192, 12288, 3072) == wide
     assert w8.w8a8_gemm_select_config(8192, 12160, 3072) != wide   # N not a multiple of 384
     assert w8.w8a8_gemm_select_config(8192, 12288, 3000) != wide   # K not a multiple of 64
+    # the K-split ping-pong tile: the measured choice for the 1024px
+    # down-projection only (the cost model never takes it)
+    ksplit = names.index("bm256_bn192_bk64_s5_mf16_ppk")
+    assert w8.w8a8_gemm_select_config(4096, 3072, 12288) == ksplit
+    assert w8.w8a8_gemm_select_config(8192, 3072, 12288) != ksplit
+    assert w8.w8a8_gemm_select_config(4096, 3072, 6144) != ksplit
 
 
 def test_fp8_entry_validation():

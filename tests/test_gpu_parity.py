@@ -260,6 +260,32 @@ def test_wide_pingpong_tile_whole_tiles(M, N, K, with_bias):
     assert np.array_equal(bits(y), want)
 
 
+# The K-split ping-pong kernel (configuration 15) on shapes of whole 256 x 192
+# tiles: one tile at the minimum depth (K = 256: two k-steps per group),
+# four tiles, 256 tiles (one per workgroup, the 1024px down-projection's grid
+# at a short K) and 288 tiles (workgroups that run a second tile after
+# draining the first), each bit-exact against the oracle with and without a
+# bias.
+@pytest.mark.parametrize("M,N,K", [(256, 192, 256), (512, 384, 384), (4096, 3072, 512),
+                                   (4608, 3072, 256)])
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_ksplit_pingpong_whole_tiles(M, N, K, with_bias):
+    rng = np.random.default_rng(3 * M + N + K + with_bias)
+    xb = rand_bits(rng, M, K, outliers=max(1, K // 100))
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    bb = rand_bits(rng, 1, N, scale=0.1)[0] if with_bias else None
+    wq, sw = w8.w8a8_quantize_weight(torch.from_numpy(w).to(DEV))
+    wqo, swo = oracle.quantize_rows_f32(w)
+    assert np.array_equal(host(wq), wqo) and np.array_equal(host(sw), swo)
+    want = oracle.linear(xb, wqo, swo, bb)["y"]
+    q, s = w8.w8a8_quantize_act(dev_bf16(xb))
+    bias = dev_bf16(bb) if with_bias else None
+    cfg = [c for c in range(ncfg()) if w8.w8a8_gemm_config_name(c) == "bm256_bn192_bk64_s5_mf16_ppk"]
+    assert len(cfg) == 1
+    y = w8.w8a8_gemm_ex(q, s, wq, sw, bias, config=cfg[0])
+    assert np.array_equal(bits(y), want)
+
+
 def _at_offset(t: torch.Tensor, k: int) -> torch.Tensor:
     """A copy of 1-D t that starts k elements into a fresh allocation."""
     big = torch.zeros(t.numel() + k, dtype=t.dtype, device=DEV)

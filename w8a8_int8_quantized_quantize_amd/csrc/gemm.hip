@@ -1407,6 +1407,152 @@ __global__ __launch_bounds__(C::kThreads) void gemm_pp_kernel(GemmArgs a, int T,
   if (grp == 0) block_barrier();
 }
 
+// Ping-pong over K (configuration 15, the 1024px down-projection).  Two groups
+// of four waves each hold the whole BM x BN tile (wave tiles TM x TN, as in
+// the 4-wave kernel) and take alternate k-steps: interval t is group t % 2's
+// memory phase for k-step t (its fragment reads, and its refill of stage
+// t + S - 1 into the buffer stage t - 1 used) while the other group runs the
+// MFMAs of k-step t - 1.  The ring has an odd number of stages S, so the group
+// that refills a buffer is the group that reads it next and each wave waits
+// for its own loads only.  At the end of a tile (no chaining: every load is
+// drained) group 1 hands its partial sums to group 0 through LDS, and group 0
+// writes the epilogue.  Shapes of whole tiles with K a multiple of 2 BK and at
+// least 4 BK; int32 sums are exact, so the output bits equal the 4-wave
+// kernel's.
+template <class C>
+__global__ __launch_bounds__(2 * C::kThreads) void gemm_ppk_kernel(GemmArgs a, int T, int MTi, int NTi) {
+  static_assert(C::kWaves == 4 && C::WN == 2 && C::kSteps == 1 && C::MF == 16 && C::kEpiLds &&
+                C::STAGES % 2 == 1 && C::FM % 2 == 0, "K-split ping-pong tile");
+  constexpr int S = C::STAGES;
+  constexpr int L = C::kLoadsPerWave;
+  static_assert(4 * C::FN * 2 * 1024 <= S * C::kStage, "exchange area");
+  __shared__ __attribute__((aligned(1024))) int8_t smem[S * C::kStage + C::kEpiBytes];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int grp = wave / 4, w4 = wave % 4;
+  const int wm = w4 / C::WN, wn = w4 % C::WN;
+  int t = blockIdx.x;
+  if (t >= T) return;
+  const int KST = static_cast<int>(a.K / C::BK);  // even, >= 4 (host)
+  const int KH = KST / 2;
+  // fragment addresses: lx per lane; the weight fragments sit a uniform
+  // distance below (one register fewer across the K loop)
+  uint32_t lx;
+  {
+    const int fr = lane % C::MF, fq = lane / C::MF;
+    const uint32_t l = static_cast<uint32_t>(fr * C::BK + swz<C::kSlots, C::kSwzR1>(fr, piece_chunk<C::MF, false, C::kSwzR1>(fq, 0)) * 16);
+    lx = l + static_cast<uint32_t>(C::BN * C::BK + wm * C::TM * C::BK);
+  }
+  const uint32_t dwx = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(C::BN * C::BK + wm * C::TM * C::BK - wn * C::TN * C::BK));
+  typename C::Acc acc[C::FN][C::FM];
+  Frags<C> f;
+  for (; t < T; t += static_cast<int>(gridDim.x)) {
+    int tm, tn;
+    tile_coords(t, T, MTi, NTi, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * C::BM, n0 = static_cast<int64_t>(tn) * C::BN;
+    // stage loads: block j of a stage (as in Loader) from two scalar bases,
+    // the row and k offsets added per load (no per-block 64-bit addresses
+    // kept across the K loop)
+    const global_i8* bw = sgpr_gptr(a.qw + n0 * a.K);
+    const global_i8* bx = sgpr_gptr(a.qx + m0 * a.K);
+    auto dma = [&](int st, int8_t* dst) {
+      // the lane's offset, recomputed per call (not kept across the K loop)
+      int lnr = lane;
+      asm volatile("" : "+v"(lnr));
+      const uint32_t loff = static_cast<uint32_t>((lnr / C::kSlots) * a.K +
+                                                  swz<C::kSlots, C::kSwzR1>(lnr / C::kSlots, lnr % C::kSlots) * 16);
+#pragma unroll
+      for (int jj = 0; jj < L; ++jj) {
+        const int j = w4 + jj * C::kWaves;
+        constexpr int KWB = C::BN / C::kRowsPerLoad / C::kWaves;
+        const bool is_w = jj < KWB;  // compile-time after unrolling
+        const int row0 = is_w ? j * C::kRowsPerLoad : j * C::kRowsPerLoad - C::BN;
+        uint32_t off = loff + static_cast<uint32_t>(row0 * a.K + st * C::BK);
+        asm volatile("" : "+v"(off));
+        __builtin_amdgcn_global_load_lds((is_w ? bw : bx) + off, (lds_void*)(dst + j * 1024), 16, 0, 0);
+      }
+    };
+    // prologue: this group's stages grp and grp + 2 (of the first S - 1)
+#pragma unroll
+    for (int p = 0; p < (S - 1) / 2; ++p) {
+      const int st = grp + 2 * p;
+      dma(st < KST ? st : KST - 1, smem + __builtin_amdgcn_readfirstlane((st % S) * C::kStage));
+    }
+    wait_vm<((S - 1) / 2 - 1) * L>();  // this wave's first stage
+    block_barrier();                    // everyone's
+    if (grp == 1) block_barrier();      // group 1 runs one interval behind
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) acc[i][j] = typename C::Acc{};
+    for (int i = 0; i < KH; ++i) {
+      const int j = 2 * i + grp;  // this group's k-step
+      // ---- memory phase
+      sched_fence();
+      // buffer offsets as scalars: computed as vector values they took the
+      // registers the K loop does not have
+      const int8_t* cur = smem + __builtin_amdgcn_readfirstlane((j % S) * C::kStage);
+#pragma unroll
+      for (int q = 0; q < C::FM; ++q) f.x[q] = load_frag<C>(cur, lx + q * C::MF * C::BK);
+#pragma unroll
+      for (int q = 0; q < C::FN; ++q) f.w[q] = load_frag<C>(cur, lx - dwx + q * C::MF * C::BK);
+      if (i == 0 && grp == 0) stage_epilogue_vectors<C>(a, smem, m0, n0, w4, lane);
+      {
+        const int rs = j + S - 1;  // this group's stage, into the buffer stage j - 1 used
+        dma(rs < KST ? rs : KST - 1, smem + __builtin_amdgcn_readfirstlane((rs % S) * C::kStage));
+      }
+      block_barrier();
+      // ---- compute phase
+      sched_fence();
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int fi = 0; fi < C::FN; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < C::FM; ++fj) acc[fi][fj] = C::Op::run(f.w[fi], f.x[fj], acc[fi][fj]);
+      __builtin_amdgcn_s_setprio(0);
+      sched_fence();
+      // this group's next stage (j + 2, issued one own step earlier) landed
+      wait_vm<((S - 1) / 2 - 1) * L>();
+      block_barrier();
+    }
+    if (grp == 0) block_barrier();  // group 1 passed one barrier more
+    wait_vm0();                     // the trailing repeated stages
+    block_barrier();
+    // group 1 hands its partial sums to group 0 (the wave at the same tile
+    // position) through LDS, two activation blocks at a time
+#pragma unroll
+    for (int r = 0; r < C::FM / 2; ++r) {
+      if (grp == 1) {
+        v4i* mine = reinterpret_cast<v4i*>(smem + w4 * (C::FN * 2 * 1024));
+#pragma unroll
+        for (int fi = 0; fi < C::FN; ++fi)
+#pragma unroll
+          for (int fj = 0; fj < 2; ++fj)
+            mine[(fi * 2 + fj) * 64 + lane] = __builtin_bit_cast(v4i, acc[fi][2 * r + fj]);
+      }
+      block_barrier();
+      if (grp == 0) {
+        const v4i* theirs = reinterpret_cast<const v4i*>(smem + w4 * (C::FN * 2 * 1024));
+#pragma unroll
+        for (int fi = 0; fi < C::FN; ++fi)
+#pragma unroll
+          for (int fj = 0; fj < 2; ++fj) {
+            const v4i o = theirs[(fi * 2 + fj) * 64 + lane];
+            acc[fi][2 * r + fj] += __builtin_bit_cast(typename C::Acc, o);
+          }
+      }
+      block_barrier();
+    }
+    if (grp == 0) {
+      int ln2 = lane, wv2 = w4;
+      asm volatile("" : "+v"(ln2), "+s"(wv2));
+      epilogue_fast<C, true>(a, m0, n0, wv2 % C::WN, wv2 / C::WN, ln2, acc, smem);
+    }
+    block_barrier();  // the epilogue vectors and stages are free again
+  }
+}
+
 // ----------------------------------------------------------- few tokens --
 // A GEMM with a handful of token rows is bound by streaming the weights from
 // HBM once (M = 1 .. 16: 2 .. 32 ops per weight byte).  Each workgroup owns
@@ -1949,6 +2095,7 @@ using C9 = Tile<256, 256, 2, 2, 64, 4, 16>;   // C0 on 16x16x64 blocks, one k-st
 using C10 = Tile<256, 192, 2, 2, 64, 4, 16>;  // C7 on 16x16x64 blocks
 using C11 = Tile<256, 256, 2, 4, 64, 4, 16>;  // C9 with 8 waves (2 per SIMD), wave tile 128 x 64
 using C14 = Tile<256, 384, 2, 4, 64, 3, 16>;  // 8 waves, wave tile 128 x 96, 3 stages of 40 KiB
+using C15 = Tile<256, 192, 2, 2, 64, 5, 16>;  // C10's wave tiles, 5 stages, twice the waves (K split)
 // configuration 12: C11's tile on the ping-pong kernel (gemm_pp_kernel) for
 // interior tiles; its edge tiles, and shapes with K < STAGES x BK, take C11's
 // own kernels
@@ -1965,6 +2112,10 @@ using C14 = Tile<256, 384, 2, 4, 64, 3, 16>;  // 8 waves, wave tile 128 x 96, 3 
 // tiles (M a multiple of 256, N of 384, K of 64 with at least 3 stages,
 // aligned vectors) with bf16 output; anything else, int32 output included,
 // takes configuration 12's path.
+// configuration 15: the K-split ping-pong kernel (gemm_ppk_kernel) on C10's
+// 256 x 192 tile: two groups of four 128 x 96 wave tiles take alternate
+// k-steps, so that one wave per SIMD issues MFMAs while the other loads; for
+// the 1024px down-projection (one tile per workgroup), a measured choice only
 
 const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf32", 256, 256, 256, 1, 0.97f},
@@ -1982,12 +2133,14 @@ const ConfigInfo kConfigs[] = {
     {"bm256_bn256_bk64_s4_mf16_pp", 256, 256, 512, 1, 1.05f},
     {"rows64_bn48_splitk8_mf16", 64, 48, 512, 1, 0.30f},
     {"bm256_bn384_bk64_s3_mf16_pp", 256, 384, 512, 1, 1.14f},
+    {"bm256_bn192_bk64_s5_mf16_ppk", 256, 192, 512, 1, 0.95f},
 };
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 constexpr int kSkinny = 6;    // 16-row tiled kernel
 constexpr int kFewRows = 8;   // split-K few-row kernel
 constexpr int kRowBlocks = 13;  // split-K kernel on 64-row blocks
 constexpr int kPpWide = 14;     // 256 x 384 ping-pong tile, whole tiles only
+constexpr int kPpK = 15;        // K-split ping-pong on 256 x 192 tiles
 constexpr int kNumCU = 256;  // MI355X compute units (tile-wave estimate)
 
 // Persistent grid: as many workgroups of `kernel` as fit on the device at
@@ -2106,6 +2259,27 @@ hipError_t launch_pp(const GemmArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
+// Configuration 15, bf16 output: the K-split ping-pong kernel when the shape
+// is whole 256 x 192 tiles with K a multiple of 128 and at least 256 (and
+// aligned vectors), else configuration 10's path (the same output bits).
+hipError_t launch_ppk(const GemmArgs& a, hipStream_t stream) {
+  using C = C15;
+  const bool ok = a.M > 0 && a.N > 0 && a.M % C::BM == 0 && a.N % C::BN == 0 &&
+                  a.K % (2 * C::BK) == 0 && a.K >= 4 * C::BK &&
+                  reinterpret_cast<uintptr_t>(a.sw) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(a.sx) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(a.bias) % 16 == 0;
+  if (!ok) return launch_cfg<C10, false>(a, stream);
+  const int64_t MTi = a.M / C::BM, NTi = a.N / C::BN, Ti = MTi * NTi;
+  if (Ti > INT32_MAX) return hipErrorInvalidValue;
+  int grid = 0;
+  hipError_t e = persistent_grid<gemm_ppk_kernel<C>>(2 * C::kThreads, Ti, grid);
+  if (e != hipSuccess) return e;
+  gemm_ppk_kernel<C><<<dim3(grid), dim3(2 * C::kThreads), 0, stream>>>(
+      a, static_cast<int>(Ti), static_cast<int>(MTi), static_cast<int>(NTi));
+  return hipGetLastError();
+}
+
 // Whole 256 x 384 tiles for the wide ping-pong configuration (vector
 // alignment is checked at launch).
 bool pp_wide_covers(int64_t M, int64_t N, int64_t K) {
@@ -2171,7 +2345,7 @@ const MeasuredChoice kMeasured[] = {
     {2304, 3072, 3072, 3},     // 768px attention projection: bm128_bn256_bk128_s3_mf32
     {2304, 9216, 3072, 14},    // 768px fused QKV: bm256_bn384_bk64_s3_mf16_pp
     {4096, 12288, 3072, 14},   // 1024px MLP up: bm256_bn384_bk64_s3_mf16_pp
-    {4096, 3072, 12288, 10},   // 1024px MLP down: bm256_bn192_bk64_s4_mf16
+    {4096, 3072, 12288, 15},   // 1024px MLP down: bm256_bn192_bk64_s5_mf16_ppk
     {1, 18432, 3072, 8},       // few_rows_splitk4_mf16
     {1, 3072, 3072, 8},
     {16, 18432, 3072, 8},
@@ -2213,7 +2387,7 @@ int gemm_select_config(int64_t M, int64_t N, int64_t K) {
   double best_cost = 1e300;
   for (int c = 0; c < kNumConfigs; ++c) {
     if (c == kSkinny || c == kFewRows) continue;  // chosen above for M <= 16
-    if (c == kRowBlocks) continue;  // measured choice only
+    if (c == kRowBlocks || c == kPpK) continue;  // measured choices only
     if (c == kPpWide && !pp_wide_covers(M, N, K)) continue;  // else configuration 12's path
     const ConfigInfo& ci = kConfigs[c];
     const int64_t tiles = ((M + ci.BM - 1) / ci.BM) * ((N + ci.BN - 1) / ci.BN);
@@ -2388,6 +2562,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool out_int32, int cfg, hipStream_t s
     case 13: return out_int32 ? launch_few_rows_st<8, 3, true, 1, false, false, 4, true, true>(a, stream)
                               : launch_few_rows_st<8, 3, false, 1, false, false, 4, true, true>(a, stream);
     case 14: return out_int32 ? launch_pp<C11, true>(a, stream) : launch_pp_wide(a, stream);
+    case 15: return out_int32 ? launch_cfg<C10, true>(a, stream) : launch_ppk(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
