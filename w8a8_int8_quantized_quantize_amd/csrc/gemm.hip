@@ -206,14 +206,15 @@ constexpr int kFastStores = (C::Op::kGroups % 2 == 0 || (C::MF == 16 && C::FM % 
                                 : C::FM * C::FN * C::Op::kGroups;
 
 // Map a linear tile index to (tile_m, tile_n): XCD-contiguous ranges, then
-// grouped order inside a range.
+// grouped order inside a range (groups of GM M-tiles).
+template <int GM = kGroupM>
 __device__ __forceinline__ void tile_coords(int t, int T, int MT, int NT, int& tm, int& tn) {
   const int per = T / 8;
   if (t < per * 8) t = (t % 8) * per + t / 8;
-  const int width = kGroupM * NT;
+  const int width = GM * NT;
   const int group = t / width;
-  const int first_m = group * kGroupM;
-  const int gsz = min(MT - first_m, kGroupM);
+  const int first_m = group * GM;
+  const int gsz = min(MT - first_m, GM);
   const int r = t - group * width;
   tm = first_m + r % gsz;
   tn = r / gsz;
@@ -1449,7 +1450,11 @@ __global__ __launch_bounds__(2 * C::kThreads) void gemm_ppk_kernel(GemmArgs a, i
   Frags<C> f;
   for (; t < T; t += static_cast<int>(gridDim.x)) {
     int tm, tn;
-    tile_coords(t, T, MTi, NTi, tm, tn);
+    // groups of 4 M-tiles: on the 1024px down-projection (16 x 16 tiles, one
+    // per workgroup) each XCD takes a 4 x 8 block, whose 4 activation and 8
+    // weight panels (31.5 MB at K = 12288) are fewer bytes than the 8 x 4
+    // block's (34.6 MB); measured 2% faster than groups of 8, same bits
+    tile_coords<4>(t, T, MTi, NTi, tm, tn);
     const int64_t m0 = static_cast<int64_t>(tm) * C::BM, n0 = static_cast<int64_t>(tn) * C::BN;
     // stage loads: block j of a stage (as in Loader) from two scalar bases,
     // the row and k offsets added per load (no per-block 64-bit addresses
